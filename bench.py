@@ -1,0 +1,443 @@
+"""Throughput of the speculative verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of the library on one batch of synthetic inputs already resident in
+HBM.  The default workload is linear speculative sampling with B=64 sequences, k=5
+draft tokens and a 32000-token bfloat16 vocabulary; the metric is verified draft
+positions per second (B*k per step).  Other workloads (--workload) print their own line.
+
+Inputs are rotated over enough device copies (>= 1 GiB in total by default) that the
+256 MB Infinity Cache cannot serve a step from the previous step's reads.  Timing uses
+HIP events recorded on the stream the kernels run on, around exactly K steps, with a
+device synchronisation on both sides.  The JSON line carries a roofline block for the
+dominant kernel (algorithmic bytes per launch / average launch time, against 8 TB/s)
+and the CPU oracle timed on a bounded sample of the same workload on host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["speculative_sampling_verify_03_amd/csrc/verify_rows.hip",
+                  "speculative_sampling_verify_03_amd/csrc/verify_greedy.hip",
+                  "speculative_sampling_verify_03_amd/csrc/lmhead_gemm.hip",
+                  "speculative_sampling_verify_03_amd/csrc/sv_device.hpp"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="linear-b64-k5-v32000",
+                    choices=["linear-b64-k5-v32000", "linear-b1-k4-v1024", "linear-b1000-k4-v1024",
+                             "linear-b256-k8-v128256", "greedy-b256-k8-v128256", "tree-b16-n61-v128256",
+                             "lmhead-b32-k5-h8192-v128256", "copy-probe"])
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- workloads
+class Linear:
+    ws_kind = 0  # SV_KIND_LINEAR
+
+    def __init__(self, name, make_case, seeds, dtype_name, temperature):
+        self.name = name
+        self.make_case = make_case
+        self.seeds = seeds
+        self.dtype_name = dtype_name
+        self.T = temperature
+
+    def setup(self, sv, torch, rotate_bytes):
+        self.sv = sv
+        self.torch = torch
+        self.cases = [self.make_case(s) for s in self.seeds]
+        c0 = self.cases[0]
+        self.B, self.R, self.V = c0.logits.shape
+        self.k = self.R - 1
+        per_set = c0.logits.numel() * c0.logits.element_size() + c0.draft_probs.numel() * c0.draft_probs.element_size()
+        nsets = max(len(self.cases), int(np.ceil(rotate_bytes / per_set)))
+        self.sets = []
+        for i in range(nsets):
+            c = self.cases[i % len(self.cases)]
+            self.sets.append((c.logits.cuda(), c.draft_probs.cuda(), c.draft_tokens.cuda(), i % len(self.cases)))
+        self.tokens = torch.empty((self.B, self.R), dtype=torch.int32, device="cuda")
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device="cuda")
+        self.ws = sv.new_workspace(self.ws_kind, self.B, self.k, self.V)
+        self.resident_bytes = per_set * nsets
+        # realised rejections per distinct input (compulsory q-row reads)
+        self.rejected = []
+        for lg, q, x, _ in self.sets[:len(self.cases)]:
+            self.launch_set(lg, q, x)
+            torch.cuda.synchronize()
+            self.rejected.append(int((self.alen < self.k).sum()))
+
+    def launch_set(self, lg, q, x):
+        self.sv.spec_verify_linear(lg, q, x, self.T, 0, 0, self.tokens, self.alen, None, None, self.ws)
+
+    def launch(self, i):
+        lg, q, x, _ = self.sets[i % len(self.sets)]
+        self.launch_set(lg, q, x)
+
+    def positions(self):
+        return self.B * self.k
+
+    def algorithmic_bytes(self):
+        c0 = self.cases[0]
+        el = c0.logits.element_size()
+        eq = c0.draft_probs.element_size()
+        rej = float(np.mean(self.rejected))
+        return (self.B * self.R * self.V * el          # every target logit row once
+                + rej * self.V * eq                     # the draft row at each rejection
+                + self.B * self.k * (eq + 4)            # q(x) gathers and draft tokens
+                + self.B * self.R * 4 + self.B * 4)     # outputs
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_len": self.k, "vocab": self.V,
+                "logits_dtype": self.dtype_name, "temperature": self.T}
+
+    def oracle_sample(self, budget_s):
+        from oracle import verify_linear
+        from synthetic import to_numpy_f64
+        c = self.cases[0]
+        L = to_numpy_f64(c.logits)
+        Q = to_numpy_f64(c.draft_probs)
+        X = c.draft_tokens.numpy()
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            b = done % self.B
+            verify_linear(L[b:b + 1], Q[b:b + 1], X[b:b + 1], self.T, 0, 0)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        return done * self.k / el, f"{done} sequences of the first input batch ({done * self.k} positions), one at a time"
+
+
+class Greedy(Linear):
+    def launch_set(self, lg, q, x):
+        self.sv.spec_verify_greedy(lg, x, self.tokens, self.alen, self.ws)
+
+    ws_kind = 1  # SV_KIND_GREEDY
+
+    def setup(self, sv, torch, rotate_bytes):
+        super().setup(sv, torch, rotate_bytes)
+        self.sets = [(lg, q, self.cases[ci].greedy_tokens.cuda(), ci) for lg, q, x, ci in self.sets]
+
+    def algorithmic_bytes(self):
+        el = self.cases[0].logits.element_size()
+        return self.B * self.R * self.V * el + self.B * self.k * 4 + self.B * self.R * 4 + self.B * 4
+
+    def oracle_sample(self, budget_s):
+        from oracle import verify_greedy
+        from synthetic import to_numpy_f64
+        c = self.cases[0]
+        L = to_numpy_f64(c.logits)
+        X = c.greedy_tokens.numpy()
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            b = done % self.B
+            verify_greedy(L[b:b + 1], X[b:b + 1])
+            done += 1
+        el = time.perf_counter() - t0
+        return done * self.k / el, f"{done} sequences, one at a time"
+
+
+class Tree:
+    def __init__(self, name, seeds):
+        self.name = name
+        self.seeds = seeds
+
+    def setup(self, sv, torch, rotate_bytes):
+        from synthetic import cfg5_case
+        self.sv = sv
+        self.torch = torch
+        self.cases = [cfg5_case(seed=s) for s in self.seeds]
+        c0 = self.cases[0]
+        self.B, self.N, self.V = c0.logits.shape
+        self.par = c0.parents.tolist()
+        depth = [0] * self.N
+        for c in range(1, self.N):
+            depth[c] = depth[self.par[c]] + 1
+        self.D = max(depth)
+        per_set = c0.logits.numel() * 2 + c0.draft_probs.numel() * 2
+        nsets = max(len(self.cases), int(np.ceil(rotate_bytes / per_set)))
+        self.sets = [(self.cases[i % len(self.cases)].logits.cuda(), self.cases[i % len(self.cases)].draft_probs.cuda(),
+                      self.cases[i % len(self.cases)].node_tokens.cuda()) for i in range(nsets)]
+        self.tokens = torch.empty((self.B, self.D + 1), dtype=torch.int32, device="cuda")
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device="cuda")
+        self.path = torch.empty((self.B, self.D + 1), dtype=torch.int32, device="cuda")
+        self.ws = sv.new_workspace(sv.SV_KIND_TREE, self.B, self.N, self.V)
+        self.resident_bytes = per_set * nsets
+
+    def launch(self, i):
+        lg, q, t = self.sets[i % len(self.sets)]
+        self.sv.spec_verify_tree(lg, q, t, self.par, 1.0, 0, 0, self.tokens, self.alen, self.path, self.ws)
+
+    def positions(self):
+        return self.B * (self.N - 1)
+
+    def algorithmic_bytes(self):
+        return (self.B * self.N * self.V * 2 + self.B * (self.N - 1) * (2 + 4)
+                + self.B * (self.D + 1) * 8 + self.B * 4)
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "tree_nodes": self.N, "vocab": self.V,
+                "logits_dtype": "bf16", "temperature": 1.0}
+
+    def oracle_sample(self, budget_s):
+        from oracle import verify_tree
+        from synthetic import to_numpy_f64
+        c = self.cases[0]
+        L = to_numpy_f64(c.logits)
+        Q = to_numpy_f64(c.draft_probs)
+        T_ = c.node_tokens.numpy()
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            b = done % self.B
+            verify_tree(L[b:b + 1], Q[b:b + 1], T_[b:b + 1], c.parents, 1.0, 0, 0)
+            done += 1
+        el = time.perf_counter() - t0
+        return done * (self.N - 1) / el, f"{done} sequences, one at a time"
+
+
+class LMHead:
+    name = "lmhead-b32-k5-h8192-v128256"
+
+    def setup(self, sv, torch, rotate_bytes):
+        from synthetic import cfg4_case
+        self.sv = sv
+        self.torch = torch
+        self.case = cfg4_case()
+        c = self.case
+        self.B, self.R, self.H = c.hidden.shape
+        self.k = self.R - 1
+        self.V = c.weight.shape[1]
+        self.h = c.hidden.cuda()
+        self.w = c.weight.cuda()  # 2.1 GB: larger than every cache level on its own
+        self.q = c.draft_probs.cuda()
+        self.x = c.draft_tokens.cuda()
+        self.logits = torch.empty((self.B, self.R, self.V), dtype=torch.float32, device="cuda")
+        self.tokens = torch.empty((self.B, self.R), dtype=torch.int32, device="cuda")
+        self.alen = torch.empty((self.B,), dtype=torch.int32, device="cuda")
+        self.ws = sv.new_workspace(sv.SV_KIND_LMHEAD, self.B, self.k, self.V, self.H)
+        self.ws2 = sv.new_workspace(sv.SV_KIND_LINEAR, self.B, self.k, self.V)
+        self.resident_bytes = self.w.numel() * 2
+        self.launch(0)
+        torch.cuda.synchronize()
+        self.rejected = int((self.alen < self.k).sum())
+
+    def launch(self, i):
+        self.sv.spec_lmhead_verify(self.h, self.w, self.q, self.x, 1.0, 0, i, self.logits, self.tokens,
+                                   self.alen, None, None, self.ws)
+
+    def launch_verify_only(self, i):
+        self.sv.spec_verify_linear(self.logits, self.q, self.x, 1.0, 0, i, self.tokens, self.alen, None, None,
+                                   self.ws2)
+
+    def positions(self):
+        return self.B * self.k
+
+    def gemm_bytes(self):
+        M = self.B * self.R
+        return self.H * self.V * 2 + M * self.H * 2 + M * self.V * 4
+
+    def gemm_flops(self):
+        return 2.0 * self.B * self.R * self.H * self.V
+
+    def algorithmic_bytes(self):
+        return self.gemm_bytes() + self.rejected * self.V * 2 + self.B * self.k * 6 + self.B * self.R * 4
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "draft_len": self.k, "hidden": self.H, "vocab": self.V,
+                "weight_dtype": "bf16", "temperature": 1.0}
+
+    def oracle_sample(self, budget_s):
+        from oracle import verify_lmhead
+        from synthetic import to_numpy_f64
+        c = self.case
+        hid = to_numpy_f64(c.hidden[:1])
+        Q = to_numpy_f64(c.draft_probs[:1])
+        X = c.draft_tokens[:1].numpy()
+        t0 = time.perf_counter()
+        done = 0
+        W = None
+        while time.perf_counter() - t0 < budget_s or done == 0:
+            if W is None:
+                W = to_numpy_f64(c.weight)
+            verify_lmhead(hid, W, Q, X, 1.0, 0, 0)
+            done += 1
+        el = time.perf_counter() - t0
+        return done * self.k / el, f"{done} sequence(s) of 6 rows, float64 GEMM + verification"
+
+
+def make_workload(name):
+    from synthetic import cfg1_case, cfg2_case, cfg3_case
+    if name == "linear-b64-k5-v32000":
+        return Linear(name, lambda s: cfg2_case(seed=s), [2, 102, 202, 302], "bf16", 1.0)
+    if name == "linear-b1-k4-v1024":
+        return Linear(name, lambda s: cfg1_case(B=1, seed=s), [1], "f32", 1.0)
+    if name == "linear-b1000-k4-v1024":
+        return Linear(name, lambda s: cfg1_case(B=1000, seed=s), [1, 101], "f32", 1.0)
+    if name == "linear-b256-k8-v128256":
+        return Linear(name, lambda s: cfg3_case(seed=s), [3], "bf16", 0.7)
+    if name == "greedy-b256-k8-v128256":
+        return Greedy(name, lambda s: cfg3_case(seed=s), [3], "bf16", 0.7)
+    if name == "tree-b16-n61-v128256":
+        return Tree(name, [5, 105])
+    if name == "lmhead-b32-k5-h8192-v128256":
+        return LMHead()
+    raise ValueError(name)
+
+
+def traffic_for(name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    rec = data.get(name)
+    if not rec or rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(torch, steps):
+    """A plain device copy of known size for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(3, steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    import speculative_sampling_verify_03_amd as sv
+    torch.cuda.set_device(0)
+    if args.workload == "copy-probe":
+        copy_probe(torch, args.steps)
+        return
+
+    wl = make_workload(args.workload)
+    wl.setup(sv, torch, args.rotate_gib * (1 << 30))
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        wl.launch(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        wl.launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    extra = {}
+    if isinstance(wl, LMHead):
+        # the GEMM dominates: its time is the step minus the verification-only time
+        torch.cuda.synchronize()
+        s2 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        s2.record(stream)
+        for i in range(args.steps):
+            wl.launch_verify_only(i)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ms_verify = s2.elapsed_time(e2) / args.steps
+        ms_gemm = ms_step - ms_verify
+        achieved = wl.gemm_bytes() / (ms_gemm * 1e-3) / 1e9
+        tflops = wl.gemm_flops() / (ms_gemm * 1e-3) / 1e12
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
+                    "kernel": "lmhead_gemm_kernel", "kernel_ms": round(ms_gemm, 4),
+                    "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+        extra["verify_ms"] = round(ms_verify, 4)
+    else:
+        achieved = wl.algorithmic_bytes() / (ms_step * 1e-3) / 1e9
+        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)"}.get(type(wl).__name__,
+                                                                                   "row_verify_kernel(linear)")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
+                    "kernel": kname, "kernel_ms": round(ms_step, 5),
+                    "algorithmic_bytes_per_launch": int(wl.algorithmic_bytes())}
+
+    value = wl.positions() / (ms_step * 1e-3)
+    cpu = None
+    if not args.no_cpu:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                cpu_value, sample = wl.oracle_sample(args.cpu_seconds)
+        except ImportError:
+            cpu_value, sample = wl.oracle_sample(args.cpu_seconds)
+        cpu = {"value": round(cpu_value, 2), "unit": "verified draft positions/s", "cores": 1, "kind": "oracle",
+               "sample": sample}
+    line = {
+        "metric": "verified draft positions/sec",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # arithmetic type: the verification kernels compute in float32 whatever the input
+        # dtype; the LM-head GEMM multiplies bf16 on the matrix cores (fp32 accumulation)
+        "dtype": "bf16" if isinstance(wl, LMHead) else "f32",
+        "data": "synthetic",
+        "config": wl.config(),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "hbm_gbs": roofline["achieved"],
+        "hbm_frac": roofline["frac"],
+        "resident_input_bytes": int(wl.resident_bytes),
+        "kernel_digest": kernel_digest(),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

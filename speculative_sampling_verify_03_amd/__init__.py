@@ -1,0 +1,22 @@
+"""MI355X (gfx950) speculative verification library: linear speculative sampling, greedy
+and static-tree verification, and an LM-head projection feeding verification, behind a
+small C ABI (include/spec_verify.h).  This package is the thin Python binding over it."""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SV_BF16,
+    SV_F32,
+    SV_KIND_GREEDY,
+    SV_KIND_LINEAR,
+    SV_KIND_LMHEAD,
+    SV_KIND_TREE,
+    SpecVerifyError,
+    library,
+    new_workspace,
+    spec_lmhead_verify,
+    spec_verify_greedy,
+    spec_verify_linear,
+    spec_verify_strerror,
+    spec_verify_tree,
+    spec_verify_workspace_bytes,
+)

@@ -1,0 +1,192 @@
+// C-ABI entry points: validate on the host, carve the caller's workspace, enqueue the
+// kernels on the caller's stream.  Nothing here allocates or synchronises.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "spec_verify.h"
+#include "sv_launch.hpp"
+#include "validate.hpp"
+
+namespace {
+
+// gfx950 check, cached per device ordinal.
+int check_device() {
+  static std::mutex mu;
+  static int state[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_E_DEVICE;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (state[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SV_E_DEVICE;
+      state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    }
+    return state[dev] == 1 ? SV_OK : SV_E_DEVICE;
+  }
+}
+
+int head_max(const void* p, int32_t V, int dt) {
+  const int eb = dt == SV_BF16 ? 2 : 4;
+  const int ve = 16 / eb;
+  if ((static_cast<int64_t>(V) * eb) % 16 == 0) return static_cast<int>((reinterpret_cast<uintptr_t>(p) & 15) / eb);
+  return ve - 1;
+}
+
+int run_rows(bool tree, const void* logits, int lt, const void* probs, int qt, const int32_t* tokens,
+             int32_t B, int32_t R, int32_t k, int32_t V, float T, uint64_t seed, uint64_t offset,
+             int32_t* out_tokens, int32_t* out_len, float* tprob, float* aprob, int32_t* out_path,
+             const sv::TreeInfo* ti, void* ws, hipStream_t st) {
+  sv::WsLayout L;
+  sv::workspace_layout(tree ? SV_KIND_TREE : SV_KIND_LINEAR, B, tree ? R : k, V, 0, &L);
+  sv::RowParams P{};
+  P.logits = logits;
+  P.probs = probs;
+  P.tokens = tokens;
+  P.B = B;
+  P.R = R;
+  P.V = V;
+  P.k = k;
+  P.q_bf16 = (qt == SV_BF16);
+  P.T = static_cast<double>(T);
+  P.c = static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+  P.seed = seed;
+  P.offset = offset;
+  P.out_tokens = out_tokens;
+  P.out_accept_len = out_len;
+  P.out_tprob = tprob;
+  P.out_aprob = aprob;
+  P.out_path = out_path;
+  P.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.counters_off);
+  P.seqword = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.seq_off);
+  P.rowword = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.row_off);
+  const bool bf16 = (lt == SV_BF16);
+  const sv::RowConfig rc = sv::choose_row_config(bf16, V, head_max(logits, V, lt));
+  P.ntiles = rc.ntiles;
+  sv::TreeDesc td{};
+  if (tree) {
+    std::memcpy(td.parent, ti->parent, 64);
+    std::memcpy(td.first_child, ti->first_child, 64);
+    std::memcpy(td.nchild, ti->nchild, 64);
+    std::memcpy(td.depth, ti->depth, 64);
+    td.N = ti->N;
+    td.D = ti->D;
+  }
+  // How the residual reads q rows (see launch_rows): every logits row must have the same
+  // 16-byte phase (whole-vector pitch), and the matching q chunks must line up with it.
+  int qmode = 0;
+  const uintptr_t la = reinterpret_cast<uintptr_t>(logits), qa = reinterpret_cast<uintptr_t>(probs);
+  if (!tree && k > 0) {
+    if (lt == qt && (static_cast<int64_t>(V) * (bf16 ? 2 : 4)) % 16 == 0 && (la & 15) == (qa & 15)) {
+      qmode = 1;
+    } else if (lt == SV_F32 && qt == SV_BF16 && (static_cast<int64_t>(V) * 4) % 16 == 0 &&
+               (static_cast<int64_t>(V) * 2) % 8 == 0 && ((qa - 2 * ((la & 15) / 4)) & 7) == 0) {
+      qmode = 2;
+    }
+  }
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_rows(P, td, bf16, tree, qmode, rc.cfg, B * R, st);
+  return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_linear(const void* target_logits, int lt, const void* draft_probs, int qt,
+                       const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V, float temperature,
+                       uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_accept_len,
+                       float* out_target_prob, float* out_accept_prob, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = sv::validate_linear(target_logits, lt, draft_probs, qt, draft_tokens, B, k, V, temperature,
+                               out_tokens, out_accept_len, workspace, workspace_bytes);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  return run_rows(false, target_logits, lt, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature,
+                  seed, offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr,
+                  nullptr, workspace, static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_greedy(const void* target_logits, int lt, const int32_t* draft_tokens, int32_t B, int32_t k,
+                       int32_t V, int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = sv::validate_greedy(target_logits, lt, draft_tokens, B, k, V, out_tokens, out_accept_len,
+                               workspace, workspace_bytes);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  sv::WsLayout L;
+  sv::workspace_layout(SV_KIND_GREEDY, B, k, V, 0, &L);
+  sv::GreedyParams P{};
+  P.logits = target_logits;
+  P.tokens = draft_tokens;
+  P.B = B;
+  P.R = k + 1;
+  P.V = V;
+  P.k = k;
+  P.S = sv::greedy_splits(B, k + 1, V);
+  P.out_tokens = out_tokens;
+  P.out_accept_len = out_accept_len;
+  P.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.counters_off);
+  P.rowword = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + L.row_off);
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_greedy(P, lt == SV_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
+}
+
+int spec_verify_tree(const void* target_logits, int lt, const void* draft_probs, int qt,
+                     const int32_t* node_tokens, const int32_t* parent_host, int32_t B, int32_t N, int32_t V,
+                     float temperature, uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                     int32_t* out_accept_len, int32_t* out_path, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  sv::TreeInfo ti;
+  int rc = sv::validate_tree(target_logits, lt, draft_probs, qt, node_tokens, parent_host, B, N, V, temperature,
+                             out_tokens, out_accept_len, workspace, workspace_bytes, &ti);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  return run_rows(true, target_logits, lt, draft_probs, qt, node_tokens, B, N, 0, V, temperature, seed, offset,
+                  out_tokens, out_accept_len, nullptr, nullptr, out_path, &ti, workspace,
+                  static_cast<hipStream_t>(stream));
+}
+
+int spec_lmhead_verify(const void* hidden, const void* lm_head, const void* draft_probs, int qt,
+                       const int32_t* draft_tokens, int32_t B, int32_t k, int32_t H, int32_t V,
+                       float temperature, uint64_t seed, uint64_t offset, float* logits_out,
+                       int32_t* out_tokens, int32_t* out_accept_len, float* out_target_prob,
+                       float* out_accept_prob, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = sv::validate_lmhead(hidden, lm_head, draft_probs, qt, draft_tokens, B, k, H, V, temperature,
+                               logits_out, out_tokens, out_accept_len, workspace, workspace_bytes);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (sv::launch_lmhead_gemm(hidden, lm_head, logits_out, B * (k + 1), H, V, st) != hipSuccess)
+    return SV_E_LAUNCH;
+  return run_rows(false, logits_out, SV_F32, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature, seed,
+                  offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr, nullptr,
+                  workspace, st);
+}
+
+size_t spec_verify_workspace_bytes(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H) {
+  sv::WsLayout L;
+  if (!sv::workspace_layout(kind, B, k_or_N, V, H, &L)) return 0;
+  return L.total;
+}
+
+const char* spec_verify_strerror(int code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_E_NULL: return "a required pointer is NULL";
+    case SV_E_SHAPE: return "invalid shape (B, k+1 <= 64, N <= 64, V, H)";
+    case SV_E_DTYPE: return "dtype must be SV_F32 or SV_BF16";
+    case SV_E_TEMP: return "temperature must be finite and > 0";
+    case SV_E_TREE: return "parent array is not a BFS-ordered tree with parent[0] = -1";
+    case SV_E_WORKSPACE: return "workspace is NULL or too small";
+    case SV_E_DEVICE: return "current HIP device is not gfx950";
+    case SV_E_LAUNCH: return "kernel launch failed";
+    case SV_E_ALIGN: return "tensor pointer is misaligned for its element type";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

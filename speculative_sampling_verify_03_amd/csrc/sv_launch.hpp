@@ -1,0 +1,74 @@
+// Kernel parameter blocks and launchers shared by the kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+// Linear / tree row kernel.  R = k+1 rows per sequence (linear) or N nodes (tree).
+struct RowParams {
+  const void* logits;      // [B, R, V], float32 or bfloat16
+  const void* probs;       // linear [B, k, V], tree [B, N, V]
+  const int32_t* tokens;   // linear [B, k], tree [B, N]
+  int32_t B, R, V, k;
+  int32_t ntiles;          // tiles per row; 1 = the row stays in registers
+  int32_t q_bf16;          // probs dtype
+  float c;                 // log2(e) / T
+  double T;
+  uint64_t seed, offset;
+  int32_t* out_tokens;
+  int32_t* out_accept_len;
+  float* out_tprob;        // linear only, may be null
+  float* out_aprob;        // linear only, may be null
+  int32_t* out_path;       // tree only, may be null
+  uint32_t* counters;      // [B] arrival tickets
+  uint64_t* seqword;       // [B][2] linear: inverted (row, token) key of the earliest
+                           //     candidate, and 64 - row of the earliest rejection seen;
+                           //     tree: mask of accepted nodes (word 0)
+  uint64_t* rowword;       // [B * R] tree: candidate token + 1 of each node
+  // every word above is zero on entry and is returned to zero before the kernel ends
+};
+
+// Static tree, BFS order, at most 64 nodes; passed by value in the kernel arguments.
+struct TreeDesc {
+  int8_t parent[64];
+  int8_t first_child[64];
+  int8_t nchild[64];
+  int8_t depth[64];
+  int32_t N;
+  int32_t D;  // maximum depth
+};
+
+constexpr int kRowConfigs = 4;
+struct RowConfig {
+  int cfg;      // index into the (threads, vectors per thread) table
+  int threads;
+  int ntiles;
+};
+RowConfig choose_row_config(bool bf16, int V, int head_max);
+// qmode: 0 element-wise q reads, 1 16-byte q vectors in phase with the logits vectors,
+// 2 float32 logits with 8-byte bfloat16 q chunks in phase with them.
+hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,
+                       int grid, hipStream_t st);
+
+// Greedy kernel: grid = B * R * S workgroups (S splits per row).
+struct GreedyParams {
+  const void* logits;
+  const int32_t* tokens;
+  int32_t B, R, V, k, S;
+  int32_t* out_tokens;
+  int32_t* out_accept_len;
+  uint32_t* counters;  // [B] arrival tickets (zero on entry and exit)
+  uint64_t* rowword;   // [B * R] orderable (value, lowest index) key of each row's maximum
+};
+constexpr int kGreedyThreads = 256;
+constexpr int kGreedyUnroll = 8;
+hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t st);
+
+// LM-head GEMM: logits[M, V] (fp32) = hidden[M, H] (bf16) @ W[H, V] (bf16).
+hipError_t launch_lmhead_gemm(const void* hidden, const void* w, float* logits, int M, int H, int V,
+                              hipStream_t st);
+
+}  // namespace sv

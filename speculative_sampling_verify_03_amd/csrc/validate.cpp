@@ -1,0 +1,169 @@
+// Host-side validation of the C-ABI arguments and the workspace layout (no HIP calls).
+#include "validate.hpp"
+
+#include <cmath>
+#include <cstring>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+namespace {
+constexpr int64_t kMaxTotalRows = int64_t(1) << 22;  // B * rows: keeps grid sizes in range
+constexpr int32_t kMaxV = int32_t(1) << 26;
+
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b == 0 || a <= limit / b); }
+}  // namespace
+
+int greedy_splits(int32_t B, int32_t R, int32_t V) {
+  const int64_t rows = static_cast<int64_t>(B) * R;
+  if (rows <= 0) return 1;
+  int64_t want = (2048 + rows - 1) / rows;
+  int64_t cap = V / 4096;
+  if (cap < 1) cap = 1;
+  if (want > cap) want = cap;
+  if (want > 64) want = 64;
+  return static_cast<int>(want < 1 ? 1 : want);
+}
+
+bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H, WsLayout* out) {
+  (void)H;
+  if (B < 0 || k_or_N < 0 || V < 1) return false;
+  int64_t rows_per_seq;
+  switch (kind) {
+    case SV_KIND_LINEAR:
+    case SV_KIND_LMHEAD:
+    case SV_KIND_GREEDY:
+      rows_per_seq = static_cast<int64_t>(k_or_N) + 1;
+      break;
+    case SV_KIND_TREE:
+      rows_per_seq = k_or_N;
+      if (rows_per_seq < 1) return false;
+      break;
+    default:
+      return false;
+  }
+  if (rows_per_seq > kMaxRows) return false;
+  const size_t b = static_cast<size_t>(B);
+  out->counters_off = 0;
+  out->seq_off = round_up(b * sizeof(uint32_t));
+  out->row_off = out->seq_off + round_up(2 * b * sizeof(uint64_t));
+  out->total = out->row_off + round_up(b * static_cast<size_t>(rows_per_seq) * sizeof(uint64_t));
+  if (out->total == 0) out->total = kWsAlign;
+  return true;
+}
+
+int check_dtype(int dt) { return (dt == SV_F32 || dt == SV_BF16) ? SV_OK : SV_E_DTYPE; }
+
+int check_temperature(float T) { return (std::isfinite(T) && T > 0.0f) ? SV_OK : SV_E_TEMP; }
+
+int check_aligned(const void* p, int dt) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return (a % (dt == SV_BF16 ? 2 : 4)) == 0 ? SV_OK : SV_E_ALIGN;
+}
+
+static int check_rows(int32_t B, int64_t R, int32_t V) {
+  if (B < 0 || R < 1 || R > kMaxRows || V < 1 || V > kMaxV) return SV_E_SHAPE;
+  if (!mul_ok(B, R, kMaxTotalRows)) return SV_E_SHAPE;
+  return SV_OK;
+}
+
+static int check_ws(const void* ws, size_t ws_bytes, int kind, int32_t B, int32_t kn, int32_t V, int32_t H) {
+  WsLayout L;
+  if (!workspace_layout(kind, B, kn, V, H, &L)) return SV_E_SHAPE;
+  if (ws == nullptr || ws_bytes < L.total) return SV_E_WORKSPACE;
+  return SV_OK;
+}
+
+int validate_linear(const void* logits, int lt, const void* probs, int qt, const int32_t* tokens,
+                    int32_t B, int32_t k, int32_t V, float T, const int32_t* out_tokens,
+                    const int32_t* out_len, const void* ws, size_t ws_bytes) {
+  int rc;
+  if ((rc = check_dtype(lt)) || (rc = check_dtype(qt))) return rc;
+  if (k < 0) return SV_E_SHAPE;
+  if ((rc = check_rows(B, static_cast<int64_t>(k) + 1, V))) return rc;
+  if ((rc = check_temperature(T))) return rc;
+  if (B == 0) return SV_OK;
+  if (!logits || !out_tokens || !out_len) return SV_E_NULL;
+  if (k > 0 && (!probs || !tokens)) return SV_E_NULL;
+  if ((rc = check_aligned(logits, lt))) return rc;
+  if (k > 0 && (rc = check_aligned(probs, qt))) return rc;
+  return check_ws(ws, ws_bytes, SV_KIND_LINEAR, B, k, V, 0);
+}
+
+int validate_greedy(const void* logits, int lt, const int32_t* tokens, int32_t B, int32_t k, int32_t V,
+                    const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes) {
+  int rc;
+  if ((rc = check_dtype(lt))) return rc;
+  if (k < 0) return SV_E_SHAPE;
+  if ((rc = check_rows(B, static_cast<int64_t>(k) + 1, V))) return rc;
+  if (B == 0) return SV_OK;
+  if (!logits || !out_tokens || !out_len) return SV_E_NULL;
+  if (k > 0 && !tokens) return SV_E_NULL;
+  if ((rc = check_aligned(logits, lt))) return rc;
+  return check_ws(ws, ws_bytes, SV_KIND_GREEDY, B, k, V, 0);
+}
+
+int build_tree(const int32_t* parent, int32_t N, TreeInfo* t) {
+  if (N < 1 || N > kMaxRows) return SV_E_SHAPE;
+  if (!parent) return SV_E_NULL;
+  std::memset(t, 0, sizeof(*t));
+  if (parent[0] != -1) return SV_E_TREE;
+  t->N = N;
+  for (int c = 0; c < N; ++c) t->first_child[c] = 0;
+  int D = 0;
+  for (int c = 1; c < N; ++c) {
+    const int32_t p = parent[c];
+    if (p < 0 || p >= c) return SV_E_TREE;
+    if (c > 1 && p < parent[c - 1]) return SV_E_TREE;  // BFS order, siblings contiguous
+    if (t->nchild[p] == 0) t->first_child[p] = static_cast<int8_t>(c);
+    t->nchild[p] = static_cast<int8_t>(t->nchild[p] + 1);
+    t->parent[c] = static_cast<int8_t>(p);
+    t->depth[c] = static_cast<int8_t>(t->depth[p] + 1);
+    if (t->depth[c] > D) D = t->depth[c];
+  }
+  t->parent[0] = -1;
+  // BFS order also means depths never decrease along the array
+  for (int c = 2; c < N; ++c)
+    if (t->depth[c] < t->depth[c - 1]) return SV_E_TREE;
+  t->D = D;
+  return SV_OK;
+}
+
+int validate_tree(const void* logits, int lt, const void* probs, int qt, const int32_t* node_tokens,
+                  const int32_t* parent_host, int32_t B, int32_t N, int32_t V, float T,
+                  const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes,
+                  TreeInfo* tree) {
+  int rc;
+  if ((rc = check_dtype(lt)) || (rc = check_dtype(qt))) return rc;
+  if ((rc = check_rows(B, N, V))) return rc;
+  if ((rc = check_temperature(T))) return rc;
+  if ((rc = build_tree(parent_host, N, tree))) return rc;
+  if (B == 0) return SV_OK;
+  if (!logits || !out_tokens || !out_len) return SV_E_NULL;
+  if (N > 1 && (!probs || !node_tokens)) return SV_E_NULL;
+  if ((rc = check_aligned(logits, lt))) return rc;
+  if (N > 1 && (rc = check_aligned(probs, qt))) return rc;
+  return check_ws(ws, ws_bytes, SV_KIND_TREE, B, N, V, 0);
+}
+
+int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt, const int32_t* tokens,
+                    int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
+                    const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes) {
+  int rc;
+  if ((rc = check_dtype(qt))) return rc;
+  if (k < 0 || H < 1 || H % 64 != 0 || H > (1 << 20)) return SV_E_SHAPE;
+  if ((rc = check_rows(B, static_cast<int64_t>(k) + 1, V))) return rc;
+  if ((rc = check_temperature(T))) return rc;
+  if (B == 0) return SV_OK;
+  if (!hidden || !w || !logits_out || !out_tokens || !out_len) return SV_E_NULL;
+  if (k > 0 && (!probs || !tokens)) return SV_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(w) & 1)) return SV_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(logits_out) & 3)) return SV_E_ALIGN;
+  if (k > 0 && (rc = check_aligned(probs, qt))) return rc;
+  return check_ws(ws, ws_bytes, SV_KIND_LMHEAD, B, k, V, H);
+}
+
+}  // namespace sv

@@ -1,0 +1,54 @@
+// Host-side argument checks and workspace layout of the C ABI.  Pure C++ (no HIP), so
+// it also builds with g++ and the host sanitizers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kMaxRows = 64;   // k + 1 and N: one wave covers a sequence's rows
+constexpr size_t kWsAlign = 256;
+
+struct WsLayout {
+  size_t counters_off, seq_off, row_off, total;
+};
+
+// Workspace layout for `kind` (SV_KIND_*): arrival counters u32[B], per-sequence words
+// u64[B][2], per-row words u64[B * rows] (rows = k + 1, or N for a tree); each section
+// 256-byte aligned.
+bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H, WsLayout* out);
+// Number of workgroups each row is split over by the greedy kernel.
+int greedy_splits(int32_t B, int32_t R, int32_t V);
+
+int check_dtype(int dt);
+int check_temperature(float T);
+int check_aligned(const void* p, int dt);
+
+// Shape / pointer validation of each entry point (no device access).
+int validate_linear(const void* logits, int lt, const void* probs, int qt, const int32_t* tokens,
+                    int32_t B, int32_t k, int32_t V, float T, const int32_t* out_tokens,
+                    const int32_t* out_len, const void* ws, size_t ws_bytes);
+int validate_greedy(const void* logits, int lt, const int32_t* tokens, int32_t B, int32_t k, int32_t V,
+                    const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes);
+
+struct TreeInfo {
+  int8_t parent[64];
+  int8_t first_child[64];
+  int8_t nchild[64];
+  int8_t depth[64];
+  int32_t N;
+  int32_t D;
+};
+// Checks the parent array (parent[0] = -1, 0 <= parent[c] < c, non-decreasing) and fills
+// children ranges and depths.
+int build_tree(const int32_t* parent, int32_t N, TreeInfo* out);
+int validate_tree(const void* logits, int lt, const void* probs, int qt, const int32_t* node_tokens,
+                  const int32_t* parent_host, int32_t B, int32_t N, int32_t V, float T,
+                  const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes,
+                  TreeInfo* tree);
+int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt, const int32_t* tokens,
+                    int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
+                    const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes);
+
+}  // namespace sv

@@ -1,0 +1,576 @@
+// Row-parallel verification kernels: linear speculative sampling and static-tree
+// verification ("Accelerating Sonar through speculation", sections "Speculative
+// decoding" and "EAGLE"; "Speculative decoding explained", section "Draft and
+// verification loop").
+//
+// One workgroup owns one vocabulary row of the target logits (row j of sequence b; for a
+// tree, the row of node u).  It
+//   1. streams the row from HBM once with 16-byte loads (each wave reads contiguous 1 KB
+//      spans) and keeps it in registers when it fits one tile (NT threads x NV vectors),
+//      computing the row max and sum of exp in one online pass;
+//   2. runs the acceptance test(s) that read this row: position j's draft token
+//      (linear) or the tokens of u's children (tree);
+//   3. if the extra token may come from this row (a rejected position or the last row for
+//      linear, a node with no accepted child for the tree), draws the candidate token by
+//      inverse CDF: per-(tile, wave) totals, then inside the winning wave the slot
+//      totals, the slot's lane scan and the element walk (DPP scans throughout);
+//   4. publishes its result with one device-scope atomic and takes a ticket on its
+//      sequence's counter; the last workgroup to arrive writes the sequence's outputs.
+//      Linear: the first rejected position is the smallest candidate row, so candidates
+//      post an atomic max of the inverted key (row, token).  Tree: accepted children go
+//      into a node mask, candidates into per-node slots.
+// A single launch covers the whole step.
+
+#include "sv_device.hpp"
+#include "sv_launch.hpp"
+
+namespace sv {
+
+// Opaque use of the packed row registers: the compiler must assume they changed, so
+// values unpacked from them earlier cannot be kept alive and reused later.  Holding the
+// unpacked floats would double the register footprint of a resident row.
+template <int NV>
+__device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    asm volatile("" : "+v"(buf[i].w[0]), "+v"(buf[i].w[1]), "+v"(buf[i].w[2]), "+v"(buf[i].w[3]));
+}
+
+// QMODE selects how the residual reads the draft-probability row q:
+//   kQVec  q has the logits' dtype and 16-byte phase: the same 16-byte vector loads;
+//   kQHalf float32 logits with bfloat16 q whose 8-byte chunks line up with the logits
+//          vectors (the fused LM-head case): one 8-byte load per vector;
+//   kQElem anything else: element loads.
+constexpr int kQElem = 0, kQVec = 1, kQHalf = 2;
+
+// Occupancy target: 512-thread workgroups (rows of more than one tile) must fit two per
+// CU, so their waves are held to 128 VGPRs (4 waves per SIMD).
+template <int NT>
+struct RowOccupancy {
+  static constexpr int kWavesPerEU = NT >= 512 ? 4 : 2;
+};
+
+template <bool BF16, int NT, int NV, bool TREE, int QMODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RowOccupancy<NT>::kWavesPerEU)))
+void row_verify_kernel(RowParams P, TreeDesc td) {
+  using E = Elem<BF16>;
+  constexpr int VE = E::kPerVec;
+  constexpr int EB = E::kBytes;
+  constexpr int NW = NT / kWave;
+  constexpr int TILE = NT * NV;  // vectors per tile
+
+  // dynamic LDS, 3 x [ntiles * NW]: per-(tile, wave) softmax partials (max, scaled sum)
+  // from pass 1, and per-(tile, wave) candidate-weight totals from pass 2
+  extern __shared__ float s_dyn[];
+  const int nunits = P.ntiles * NW;
+  float* s_pm = s_dyn;
+  float* s_ps = s_dyn + nunits;
+  float* s_tot = s_dyn + 2 * nunits;
+  __shared__ int s_flag, s_y, s_last;
+  __shared__ float s_usmp;
+  __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int r = blockIdx.x;
+  const int b = r / P.R;
+  const int j = r - b * P.R;
+  const int V = P.V;
+  const float c = P.c;
+
+  const char* rowp = static_cast<const char*>(P.logits) + static_cast<size_t>(r) * V * EB;
+  const uintptr_t ra = reinterpret_cast<uintptr_t>(rowp);
+  const int h = static_cast<int>(ra & 15) / EB;  // elements before the row inside its first vector
+  const SV_GLOBAL Vec16* vrow = gptr<Vec16>(reinterpret_cast<const void*>(ra - (ra & 15)));
+  const int nvec = (V + h + VE - 1) / VE;
+  const int qeb = P.q_bf16 ? 2 : 4;
+
+  if (TREE) {  // per-lane indexing of the tree goes through LDS, not the kernel arguments
+    if (tid < 64) {
+      s_par[tid] = td.parent[tid];
+      s_fc[tid] = td.first_child[tid];
+      s_nc[tid] = td.nchild[tid];
+      s_dep[tid] = td.depth[tid];
+    }
+    __syncthreads();
+  }
+
+  // ---- acceptance-test gathers.  The draft token is loaded before the row stream and the
+  // values it indexes right after it: vector loads complete in issue order, so waiting for
+  // the token then costs nothing extra, and the row stream is not held behind the chain.
+  int g_node = -1;
+  int g_x = -1;
+  size_t g_qrow = 0;
+  if (TREE) {
+    if (tid < s_nc[j]) {
+      g_node = s_fc[j] + tid;
+      g_x = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * P.R + g_node];
+    }
+    g_qrow = static_cast<size_t>(b) * P.R + j;
+  } else {
+    if (tid == 0 && j < P.k) {
+      g_node = j;
+      g_x = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * P.k + j];
+    }
+    g_qrow = static_cast<size_t>(b) * P.k + j;
+  }
+
+  // ---- pass 1: online max / sum of 2^((l - m) c) over the row
+  bool g_valid = false;
+  float g_l = 0.f, g_q = 0.f, g_uacc = 0.f, g_usmp = 0.f;
+  Vec16 buf[NV];
+  for (int tile = 0; tile < P.ntiles; ++tile) {
+    const int v0 = tile * TILE + wid * (NV * kWave) + lane;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = v0 + i * kWave;
+      buf[i] = mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V);
+    }
+    if (tile == 0 && g_node >= 0) {
+      g_valid = (g_x >= 0 && g_x < V);
+      if (g_valid) {
+        g_l = load_elem(rowp, g_x, BF16);
+        g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
+      }
+      draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
+    }
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) tm = fmaxf(tm, E::at(buf[i], e));
+    pin_packed(buf);  // re-unpack below instead of holding 2x the row in float registers
+    const float ref = tm == -INFINITY ? 0.f : tm;  // a share of only -inf contributes 0
+    float ts = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float vs = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) vs += fast_exp2((E::at(buf[i], e) - ref) * c);
+      ts += vs;
+    }
+    wave_merge_max_sum(tm, ts, c);  // this wave's share of this tile
+    if (lane == 0) {
+      s_pm[tile * NW + wid] = tm;
+      s_ps[tile * NW + wid] = ts;
+    }
+  }
+  pin_packed(buf);  // pass 2 starts again from the packed row
+  __syncthreads();
+  // every thread merges the partials in the same order: the row's (m, Z)
+  float m = -INFINITY, Z = 0.f;
+  for (int q = 0; q < nunits; ++q) merge_max_sum(m, Z, s_pm[q], s_ps[q], c);
+
+  // ---- acceptance tests: keep x iff u_acc * q(x) < p(x), with p(x) in double
+  bool acc = false;
+  if (g_node >= 0) {
+    double px = 0.0;
+    if (g_valid) px = exp((static_cast<double>(g_l) - static_cast<double>(m)) / P.T) / static_cast<double>(Z);
+    acc = g_valid && (static_cast<double>(g_uacc) * static_cast<double>(g_q) < px);
+    if (!TREE) {
+      const size_t o = static_cast<size_t>(b) * P.k + j;
+      if (P.out_tprob) P.out_tprob[o] = static_cast<float>(px);
+      if (P.out_aprob) {
+        double ap;
+        if (g_q > 0.f) ap = px / static_cast<double>(g_q) < 1.0 ? px / static_cast<double>(g_q) : 1.0;
+        else ap = px > 0.0 ? 1.0 : 0.0;
+        P.out_aprob[o] = static_cast<float>(ap);
+      }
+    }
+  }
+  uint64_t child_acc = 0;  // tree: this node's accepted children, as node bits (wave 0)
+  uint64_t rej_dep = 0;    // linear: value returned by the rejection publish (waited on later)
+  if (TREE) {
+    if (wid == 0) {
+      child_acc = __ballot(acc) << s_fc[j];
+      if (lane == 0) s_flag = (child_acc == 0ull);
+    }
+  } else if (tid == 0) {
+    const bool rejected = !acc && j < P.k;
+    bool cand = (j == P.k) || rejected;
+    // Rows spanning several tiles publish a rejection at once (rejword holds 64 - row of
+    // the earliest rejection seen) and consult it before their costly candidate pass:
+    // only the earliest rejected row can supply the emitted token, and the earliest one
+    // never sees an earlier rejection, so skipping changes no result.  Single-tile rows
+    // neither publish nor check.
+    if (P.ntiles > 1) {
+      if (rejected) {
+        const uint64_t seen = atomic_max_u64(&P.seqword[2 * b + 1], static_cast<uint64_t>(64 - j));
+        rej_dep = seen;  // waited on before the ticket, so the reset cannot race it
+        if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+      } else if (cand) {  // the last row: any rejection makes it irrelevant
+        const uint64_t seen =
+            __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+      }
+    }
+    s_flag = cand;
+  }
+  if (tid == 0) {
+    float us = g_usmp;  // linear: thread 0 drew the pair of position j
+    if (TREE || g_node < 0) {
+      float ua;
+      draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(j), ua, us);
+    }
+    s_usmp = us;
+    s_y = -1;
+  }
+  __syncthreads();
+
+  // ---- pass 2: candidate draw from this row
+  if (s_flag) {
+    const float u_smp = s_usmp;
+    const float invZ = 1.0f / Z;
+    bool resid = !TREE && (j < P.k);
+    const char* qrowp = static_cast<const char*>(P.probs) +
+                        (static_cast<size_t>(b) * (TREE ? P.R : P.k) + j) * V * qeb;
+    const uintptr_t qa = reinterpret_cast<uintptr_t>(qrowp);
+    const SV_GLOBAL Vec16* vq = gptr<Vec16>(reinterpret_cast<const void*>(qa - (qa & 15)));
+
+    auto load_q = [&](int vi) -> Vec16 {
+      Vec16 v{};
+      if (QMODE == kQVec) v = ld16(vq, vi, resid ? nvec : 0);
+      if (QMODE == kQHalf && resid && vi < nvec) {
+        const int e0 = vi * VE - h;  // 8-byte aligned in q by the host's choice of mode
+        const uint64_t d = *gptr<uint64_t>(qrowp + static_cast<ptrdiff_t>(e0) * 2);
+        v.w[0] = static_cast<uint32_t>(d);
+        v.w[1] = static_cast<uint32_t>(d >> 32);
+      }
+      return v;
+    };
+    // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
+    // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0)
+    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w) {
+      const int e0 = vi * VE - h;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float x = fast_exp2((E::at(lv, e) - m) * c);
+        if (resid) {
+          float q;
+          if (QMODE == kQVec) q = E::at(qv, e);
+          else if (QMODE == kQHalf) q = Elem<true>::at(qv, e);
+          else q = (e0 + e >= 0 && e0 + e < V) ? load_elem(qrowp, e0 + e, P.q_bf16 != 0) : 0.f;
+          x = fmaxf(0.f, x * invZ - q);
+        }
+        w[e] = x;
+      }
+    };
+    auto reload = [&](int v0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int vi = v0 + i * kWave;
+        buf[i] = mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V);
+      }
+    };
+    // Per-vector sums of this thread's share of a tile (seg[]), each slot's total over the
+    // wave (slot_tot[], the last lane of the slot's scan) and the wave's total (their
+    // sequential sum).  The search below walks exactly these sums, so every level of the
+    // inverse CDF agrees with the level above it.  q loads go out together while
+    // registers allow (one round trip).
+    float seg[NV];
+    float slot_tot[NV];
+    auto tile_totals = [&](int v0) -> float {
+      constexpr int GQ = QMODE == kQElem ? 2 : (NT >= 512 && QMODE == kQVec) ? 8 : NV;
+      constexpr int G = NV < GQ ? NV : GQ;
+#pragma unroll
+      for (int g0 = 0; g0 < NV; g0 += G) {
+        Vec16 qv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float w[VE];
+          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w);
+          float sgm = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) sgm += w[e];
+          seg[g0 + g] = sgm;
+        }
+      }
+      float wt = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        slot_tot[i] = lane_value(wave_inclusive_scan(seg[i]), 63);
+        wt += slot_tot[i];
+      }
+      return wt;
+    };
+
+    int loaded_tile = P.ntiles - 1;  // buf holds the last tile of pass 1
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      // One loop, one copy of tile_totals: steps 0 .. ntiles-1 compute the residual totals
+      // of every tile (residual draws only; the register-resident tile first, the others
+      // re-read, mostly from cache); the last step locates the winning (tile, wave) and lets
+      // that wave recompute its sums when they are not in registers already.
+      bool empty = false;
+      double t = 0.0, before = 0.0;
+      bool clamp = false;
+      int tile_s = 0, wave_s = 0;
+      const int first = loaded_tile;
+      for (int step = resid ? 0 : P.ntiles; step <= P.ntiles; ++step) {
+        int tile;
+        bool active;
+        if (step < P.ntiles) {
+          tile = (first + step) % P.ntiles;
+          active = true;
+        } else {
+          if (resid) __syncthreads();
+          // weight of each (tile, wave) unit: the residual totals, or for a draw from p
+          // itself the pass-1 partials rescaled to the row max (nothing recomputed)
+          auto unit = [&](int q) -> float { return resid ? s_tot[q] : s_ps[q] * fast_exp2((s_pm[q] - m) * c); };
+          // every thread walks the units in the same order: S, then the winning unit
+          float S = 0.f;
+          for (int q = 0; q < nunits; ++q) S += unit(q);
+          if (S <= 0.f) {  // residual empty through rounding: draw from p itself
+            empty = true;
+            break;
+          }
+          t = static_cast<double>(u_smp) * static_cast<double>(S);
+          float cum = 0.f;
+          int star = -1, last_pos = -1;
+          for (int q = 0; q < nunits; ++q) {
+            const float uq = unit(q);
+            const float nc = cum + uq;
+            if (uq > 0.f) last_pos = q;
+            if (star < 0 && static_cast<double>(nc) > t) {
+              star = q;
+              before = cum;
+            }
+            cum = nc;
+          }
+          // Sums at different levels are rounded in different orders; when t falls past a
+          // level's total (only within rounding of a CDF boundary) take the last positive
+          // weight.
+          if (star < 0) {
+            star = last_pos;
+            clamp = true;
+          }
+          tile_s = star / NW;
+          wave_s = star - tile_s * NW;
+          tile = tile_s;
+          active = (wid == wave_s) && (tile_s != loaded_tile || !resid);
+        }
+        if (active) {
+          const int v0 = tile * TILE + wid * (NV * kWave) + lane;
+          if (tile != loaded_tile) {  // only this wave's share when locating the winner
+            reload(v0);
+            loaded_tile = tile;
+          }
+          const float wt = tile_totals(v0);
+          if (step < P.ntiles && lane == 0) s_tot[tile * NW + wid] = wt;
+        }
+      }
+      if (empty) {
+        if (!resid) break;
+        resid = false;
+        continue;
+      }
+      if (wid == wave_s) {
+        const int v0 = tile_s * TILE + wid * (NV * kWave) + lane;
+        // slot inside the wave (uniform walk over the slot totals)
+        const double t1 = t - before;
+        int istar = -1, ilast = -1;
+        float icum = 0.f, ibefore = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const float nc = icum + slot_tot[i];
+          if (slot_tot[i] > 0.f) ilast = i;
+          if (!clamp && istar < 0 && static_cast<double>(nc) > t1) {
+            istar = i;
+            ibefore = icum;
+          }
+          icum = nc;
+        }
+        if (istar < 0) {
+          istar = ilast < 0 ? 0 : ilast;
+          clamp = true;
+        }
+        // lane inside the slot: the slot's scan again (same inputs, same values)
+        float sg = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (i == istar) sg = seg[i];
+        const float scan = wave_inclusive_scan(sg);
+        const double t2 = t1 - static_cast<double>(ibefore);
+        const uint64_t hit = __ballot(static_cast<double>(scan) > t2);
+        const uint64_t pos = __ballot(sg > 0.f);
+        int lstar;
+        if (!clamp && hit) {
+          lstar = __ffsll(static_cast<long long>(hit)) - 1;
+        } else {
+          lstar = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+          clamp = true;
+        }
+        const float excl = lane_value(scan, lstar > 0 ? lstar - 1 : 0);
+        if (lane == lstar) {
+          const int vi = v0 + istar * kWave;
+          float w[VE];
+          weights(mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V), load_q(vi), vi, w);
+          const double t3 = t2 - (lstar > 0 ? static_cast<double>(excl) : 0.0);
+          int y = -1, ylast = -1;
+          float ec = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            ec += w[e];
+            if (w[e] > 0.f) {
+              ylast = e;
+              if (!clamp && y < 0 && static_cast<double>(ec) > t3) y = e;
+            }
+          }
+          if (y < 0) y = ylast;
+          s_y = vi * VE - h + y;
+        }
+      }
+      break;
+    }
+  }
+  __syncthreads();
+
+  // ---- publish this row's result, then take the sequence ticket
+  if (tid == 0) {
+    uint64_t dep = 0;
+    if (TREE) {
+      if (child_acc) dep ^= atomic_or_u64(&P.seqword[2 * b], child_acc);
+      if (s_flag) dep ^= atomic_xchg_u64(&P.rowword[r], static_cast<uint64_t>(static_cast<uint32_t>(s_y + 1)));
+    } else {
+      dep ^= rej_dep;
+      if (s_flag) {
+        const uint64_t key = (static_cast<uint64_t>(j) << 32) | static_cast<uint32_t>(s_y);
+        dep ^= atomic_max_u64(&P.seqword[2 * b], ~key);
+      }
+    }
+    after_value(dep);
+    const uint32_t prev = take_ticket(&P.counters[b]);
+    s_last = (prev == static_cast<uint32_t>(P.R - 1));
+  }
+  __syncthreads();
+  if (!s_last || wid != 0) return;
+
+  // ---- last arrival: the sequence's outputs
+  if (!TREE) {
+    const int k = P.k;
+    uint64_t best = 0;
+    if (lane == 0) {
+      best = atomic_xchg_u64(&P.seqword[2 * b], 0ull);
+      (void)atomic_xchg_u64(&P.seqword[2 * b + 1], 0ull);
+    }
+    const uint32_t blo = static_cast<uint32_t>(lane_value(static_cast<int>(best), 0));
+    const uint32_t bhi = static_cast<uint32_t>(lane_value(static_cast<int>(best >> 32), 0));
+    const uint64_t key = ~((static_cast<uint64_t>(bhi) << 32) | blo);
+    int n = static_cast<int>(key >> 32);
+    int y = static_cast<int>(static_cast<uint32_t>(key));
+    if (n < 0 || n > k) {  // no candidate posted (cannot happen: row k always posts)
+      n = k;
+      y = -1;
+    }
+    if (lane < P.R) {
+      int t = -1;
+      if (lane < n) t = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * k + lane];
+      else if (lane == n) t = y;
+      P.out_tokens[static_cast<size_t>(b) * P.R + lane] = t;
+    }
+    if (lane == 0) {
+      P.out_accept_len[b] = n;
+      reset_ticket(&P.counters[b]);
+    }
+  } else {
+    const int N = P.R;
+    uint64_t mask = 0;
+    if (lane == 0) mask = atomic_xchg_u64(&P.seqword[2 * b], 0ull);
+    const uint32_t mlo = static_cast<uint32_t>(lane_value(static_cast<int>(mask), 0));
+    const uint32_t mhi = static_cast<uint32_t>(lane_value(static_cast<int>(mask >> 32), 0));
+    const uint64_t accm = (static_cast<uint64_t>(mhi) << 32) | mlo;
+    int cand_c = -1, dep = 0, par = 0;
+    if (lane < N) {
+      cand_c = static_cast<int>(static_cast<uint32_t>(
+                   atomic_xchg_u64(&P.rowword[static_cast<size_t>(b) * N + lane], 0ull))) - 1;
+      dep = s_dep[lane];
+      par = lane == 0 ? 0 : s_par[lane];
+    }
+    uint64_t alive = 1ull;
+    for (int d = 1; d <= td.D; ++d) {
+      const bool a = lane < N && dep == d && ((accm >> lane) & 1ull) && ((alive >> par) & 1ull);
+      alive |= __ballot(a);
+    }
+    const int key = wave_max_int(((alive >> lane) & 1ull) ? dep * 64 + (63 - lane) : -1);
+    const int cstar = 63 - (key & 63);
+    const int dstar = key >> 6;
+    const int ybonus = lane_value(cand_c, cstar);
+    // ancestors of c*: lane d holds the node at depth d on the path (d <= dstar)
+    int node = -1;
+    {
+      int cur = cstar;
+      for (int d = dstar; d >= 0; --d) {
+        if (lane == d) node = cur;
+        cur = d > 0 ? s_par[cur] : 0;
+      }
+    }
+    const int W = td.D + 1;
+    const int nxt = __shfl(node, lane + 1 < kWave ? lane + 1 : kWave - 1);  // all lanes active
+    if (lane < W) {
+      int t = -1;
+      if (lane < dstar) t = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * N + nxt];
+      else if (lane == dstar) t = ybonus;
+      P.out_tokens[static_cast<size_t>(b) * W + lane] = t;
+      if (P.out_path) P.out_path[static_cast<size_t>(b) * W + lane] = lane <= dstar ? node : -1;
+    }
+    if (lane == 0) {
+      P.out_accept_len[b] = dstar;
+      reset_ticket(&P.counters[b]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch table
+template <bool BF16, int NT, int NV, bool TREE, int QMODE>
+static hipError_t launch_one(const RowParams& P, const TreeDesc& td, int grid, hipStream_t st) {
+  const size_t lds = 3 * static_cast<size_t>(P.ntiles) * (NT / kWave) * sizeof(float);
+  hipLaunchKernelGGL((row_verify_kernel<BF16, NT, NV, TREE, QMODE>), dim3(grid), dim3(NT), lds, st, P, td);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool TREE, int QMODE>
+static hipError_t launch_rows_t(const RowParams& P, const TreeDesc& td, int cfg, int grid, hipStream_t st) {
+  switch (cfg) {
+    case 0: return launch_one<BF16, 64, 4, TREE, QMODE>(P, td, grid, st);
+    case 1: return launch_one<BF16, 256, 4, TREE, QMODE>(P, td, grid, st);
+    case 2: return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
+    default: return launch_one<BF16, 512, 16, TREE, QMODE>(P, td, grid, st);
+  }
+}
+
+// Smallest (threads, vectors per thread) whose single tile holds the row; rows longer
+// than one 512 x 16 tile use several tiles of it.
+RowConfig choose_row_config(bool bf16, int V, int head_max) {
+  static const int nt[kRowConfigs] = {64, 256, 256, 512};
+  static const int nv[kRowConfigs] = {4, 4, 16, 16};
+  const int ve = bf16 ? 8 : 4;
+  const long long need = static_cast<long long>(V) + head_max;
+  RowConfig rc{};
+  for (int i = 0; i < kRowConfigs; ++i) {
+    const long long cap = static_cast<long long>(nt[i]) * nv[i] * ve;
+    if (cap >= need || i == kRowConfigs - 1) {
+      rc.cfg = i;
+      rc.threads = nt[i];
+      rc.ntiles = static_cast<int>((need + cap - 1) / cap);
+      break;
+    }
+  }
+  return rc;
+}
+
+hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,
+                       int grid, hipStream_t st) {
+  if (tree)  // the tree draws its extra token from p alone and never reads q rows
+    return bf16 ? launch_rows_t<true, true, kQElem>(P, td, cfg, grid, st)
+                : launch_rows_t<false, true, kQElem>(P, td, cfg, grid, st);
+  if (bf16)
+    return qmode == kQVec ? launch_rows_t<true, false, kQVec>(P, td, cfg, grid, st)
+                          : launch_rows_t<true, false, kQElem>(P, td, cfg, grid, st);
+  if (qmode == kQVec) return launch_rows_t<false, false, kQVec>(P, td, cfg, grid, st);
+  if (qmode == kQHalf) return launch_rows_t<false, false, kQHalf>(P, td, cfg, grid, st);
+  return launch_rows_t<false, false, kQElem>(P, td, cfg, grid, st);
+}
+
+}  // namespace sv

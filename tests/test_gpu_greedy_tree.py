@@ -1,0 +1,76 @@
+"""GPU parity of greedy verification and static-tree verification against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import announce, check_greedy, check_tree, run_greedy, run_tree
+from synthetic import (cfg3_case, cfg5_case, chain_tree_parents, eagle_tree_parents, linear_case,
+                       to_numpy_f64, tree_case)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_cfg3_greedy_full():
+    case = cfg3_case()
+    announce("greedy B=256 k=8 V=128256 bf16")
+    got = run_greedy(case.logits, case.greedy_tokens)
+    ref = check_greedy(got, case.logits, case.greedy_tokens, what="greedy B=256 k=8 V=128256")
+    announce(f"greedy mean emitted {ref['accept_len'].mean() + 1:.3f}")
+
+
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_greedy_identity(k):
+    case = linear_case(64, k, 32000, seed=k, dtype="bf16")
+    X = torch.from_numpy(np.argmax(to_numpy_f64(case.logits)[:, :k], axis=-1).astype(np.int32))
+    got = run_greedy(case.logits, X)
+    assert np.all(got["accept_len"] == k)
+    check_greedy(got, case.logits, X, what=f"greedy identity k={k}")
+
+
+@pytest.mark.parametrize("dtype,V,misalign", [("bf16", 1001, 0), ("f32", 777, 1), ("bf16", 50257, 3),
+                                              ("f32", 131072, 0), ("bf16", 5, 0)])
+def test_greedy_ragged(dtype, V, misalign):
+    case = linear_case(40, 5, V, seed=V, dtype=dtype, noise_sigma=0.05)
+    got = run_greedy(case.logits, case.greedy_tokens, misalign)
+    check_greedy(got, case.logits, case.greedy_tokens, what=f"greedy V={V} {dtype} misalign={misalign}")
+
+
+def test_greedy_ties_lowest_index():
+    V = 4096
+    L = torch.zeros((8, 4, V), dtype=torch.bfloat16)
+    L[:, :, [17, 900, 2500, 4095]] = 3.0
+    X = torch.tensor([[17, 17, 17], [900, 17, 17], [17, 2500, 17], [17, 17, 4095]] * 2, dtype=torch.int32)
+    got = run_greedy(L, X)
+    assert list(got["accept_len"][:4]) == [3, 0, 1, 2]
+    assert np.all(got["tokens"][:, 0] == 17)
+    check_greedy(got, L, X, what="greedy ties")
+
+
+def test_cfg5_tree_full():
+    case = cfg5_case()
+    announce("tree B=16 N=61 V=128256 bf16")
+    got = run_tree(case, seed=0)
+    ref = check_tree(got, case, seed=0, what="tree B=16 N=61 V=128256")
+    announce(f"tree mean accept_len {ref['accept_len'].mean():.3f}")
+
+
+@pytest.mark.parametrize("name", ["chain", "single", "wide", "deep64"])
+def test_tree_shapes(name):
+    if name == "chain":
+        par = chain_tree_parents(9)
+    elif name == "single":
+        par = np.array([-1], dtype=np.int32)
+    elif name == "wide":
+        par = eagle_tree_parents((63,), 64)
+    else:
+        par = eagle_tree_parents((2, 2, 2, 2, 2, 2), 64)
+    case = tree_case(48, par, 3000, seed=len(par), dtype="f32", noise_sigma=0.6, sample_children=True)
+    got = run_tree(case, seed=3, offset=2)
+    check_tree(got, case, seed=3, offset=2, what=f"tree {name} N={len(par)}")
+
+
+@pytest.mark.parametrize("misalign", [(1, 0), (0, 3)])
+def test_tree_ragged_misaligned(misalign):
+    case = tree_case(20, eagle_tree_parents((3, 2, 2), 64), 1003, seed=4, dtype="bf16", noise_sigma=0.8)
+    got = run_tree(case, seed=5, misalign=misalign)
+    check_tree(got, case, seed=5, what=f"tree V=1003 misalign={misalign}")
