@@ -316,19 +316,20 @@ def make_workload(name):
 
 
 def traffic_for(name):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
-    the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 counter table, if the counters were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    try:
-        data = json.load(open(path))
-    except ValueError:
-        return None
-    rec = data.get(name)
-    if not rec or rec.get("kernel_digest") != kernel_digest():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    digest = kernel_digest()
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0] == name and cells[1] == digest:
+            try:
+                return int(cells[4])
+            except ValueError:
+                return None
+    return None
 
 
 def copy_probe(torch, steps):
