@@ -29,6 +29,10 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions.  The LM-head GEMM keeps its accumulators in VGPRs: with the
+# compiler's default AGPR placement the loop-carried accumulators were shuffled between
+# register files every step, which stalls on the matrix-core results.
+HIP_FILE_FLAGS = {"lmhead_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall"]
 
 
@@ -60,7 +64,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        steps.append([hipcc, *HIP_FLAGS, *incs, "-c", os.path.join(CSRC, src), "-o", obj])
+        steps.append([hipcc, *HIP_FLAGS, *HIP_FILE_FLAGS.get(src, []), *incs, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
