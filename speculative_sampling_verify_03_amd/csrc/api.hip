@@ -62,7 +62,7 @@ int run_rows(bool tree, const void* logits, int lt, const void* probs, int qt, c
   P.seqword = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.seq_off);
   P.rowword = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.row_off);
   const bool bf16 = (lt == SV_BF16);
-  const sv::RowConfig rc = sv::choose_row_config(bf16, V, head_max(logits, V, lt));
+  const sv::RowConfig rc = sv::choose_row_config(bf16, V, head_max(logits, V, lt), static_cast<int64_t>(B) * R);
   P.ntiles = rc.ntiles;
   sv::TreeDesc td{};
   if (tree) {

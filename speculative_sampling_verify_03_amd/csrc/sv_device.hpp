@@ -45,16 +45,18 @@ __device__ __forceinline__ const SV_GLOBAL T* gptr(const void* p) {
   return (const SV_GLOBAL T*)(p);
 }
 
-// 16-byte load of vector i when 0 <= i < n, zeros otherwise.
+// 16-byte load of vector i when 0 <= i < n, zeros otherwise (n >= 1).  Branch free: lanes
+// out of range load vector 0 and discard it, so a run of ld16 calls stays in one basic
+// block and issues back to back instead of one exec-masked block (and one wait) per load.
 __device__ __forceinline__ Vec16 ld16(const SV_GLOBAL Vec16* p, int i, int n) {
-  Vec16 v{};
-  if (static_cast<unsigned>(i) < static_cast<unsigned>(n)) {
-    const SV_GLOBAL Vec16& g = p[i];
-    v.w[0] = g.w[0];
-    v.w[1] = g.w[1];
-    v.w[2] = g.w[2];
-    v.w[3] = g.w[3];
-  }
+  const bool in = static_cast<unsigned>(i) < static_cast<unsigned>(n);
+  const SV_GLOBAL Vec16& g = p[in ? i : 0];
+  const uint32_t w0 = g.w[0], w1 = g.w[1], w2 = g.w[2], w3 = g.w[3];
+  Vec16 v;
+  v.w[0] = in ? w0 : 0u;
+  v.w[1] = in ? w1 : 0u;
+  v.w[2] = in ? w2 : 0u;
+  v.w[3] = in ? w3 : 0u;
   return v;
 }
 

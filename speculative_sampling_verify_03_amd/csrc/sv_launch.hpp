@@ -47,7 +47,7 @@ struct RowConfig {
   int threads;
   int ntiles;
 };
-RowConfig choose_row_config(bool bf16, int V, int head_max);
+RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows);
 // qmode: 0 element-wise q reads, 1 16-byte q vectors in phase with the logits vectors,
 // 2 float32 logits with 8-byte bfloat16 q chunks in phase with them.
 hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,

@@ -43,11 +43,13 @@ __device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
 //   kQElem anything else: element loads.
 constexpr int kQElem = 0, kQVec = 1, kQHalf = 2;
 
-// Occupancy target: 512-thread workgroups (rows of more than one tile) must fit two per
-// CU, so their waves are held to 128 VGPRs (4 waves per SIMD).
+// Occupancy target: at least two waves per SIMD (up to 256 VGPRs).  Holding the
+// 512-thread configurations to 128 VGPRs (two workgroups per CU) spilled the linear
+// instantiations to scratch; with a whole tile's loads in flight per thread one
+// workgroup per CU already keeps enough bytes moving.
 template <int NT>
 struct RowOccupancy {
-  static constexpr int kWavesPerEU = NT >= 512 ? 4 : 2;
+  static constexpr int kWavesPerEU = 2;
 };
 
 template <bool BF16, int NT, int NV, bool TREE, int QMODE>
@@ -122,11 +124,11 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   Vec16 buf[NV];
   for (int tile = 0; tile < P.ntiles; ++tile) {
     const int v0 = tile * TILE + wid * (NV * kWave) + lane;
+    // every load of the tile is in flight before the first edge mask
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = v0 + i * kWave;
-      buf[i] = mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V);
-    }
+    for (int i = 0; i < NV; ++i) buf[i] = ld16(vrow, v0 + i * kWave, nvec);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
     if (tile == 0 && g_node >= 0) {
       g_valid = (g_x >= 0 && g_x < V);
       if (g_valid) {
@@ -230,12 +232,13 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 
     auto load_q = [&](int vi) -> Vec16 {
       Vec16 v{};
-      if (QMODE == kQVec) v = ld16(vq, vi, resid ? nvec : 0);
-      if (QMODE == kQHalf && resid && vi < nvec) {
-        const int e0 = vi * VE - h;  // 8-byte aligned in q by the host's choice of mode
+      if (QMODE == kQVec && resid) v = ld16(vq, vi, nvec);
+      if (QMODE == kQHalf && resid) {  // branch free like ld16: lanes past the row load vector 0
+        const bool in = vi < nvec;
+        const int e0 = (in ? vi : 0) * VE - h;  // 8-byte aligned in q by the host's choice of mode
         const uint64_t d = *gptr<uint64_t>(qrowp + static_cast<ptrdiff_t>(e0) * 2);
-        v.w[0] = static_cast<uint32_t>(d);
-        v.w[1] = static_cast<uint32_t>(d >> 32);
+        v.w[0] = in ? static_cast<uint32_t>(d) : 0u;
+        v.w[1] = in ? static_cast<uint32_t>(d >> 32) : 0u;
       }
       return v;
     };
@@ -258,10 +261,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     };
     auto reload = [&](int v0) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int vi = v0 + i * kWave;
-        buf[i] = mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V);
-      }
+      for (int i = 0; i < NV; ++i) buf[i] = ld16(vrow, v0 + i * kWave, nvec);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
     };
     // Per-vector sums of this thread's share of a tile (seg[]), each slot's total over the
     // wave (slot_tot[], the last lane of the slot's scan) and the wave's total (their
@@ -275,9 +277,11 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       constexpr int G = NV < GQ ? NV : GQ;
 #pragma unroll
       for (int g0 = 0; g0 < NV; g0 += G) {
-        Vec16 qv[G];
+        Vec16 qv[G] = {};
+        if (resid) {  // one uniform branch around the whole batch of q loads
 #pragma unroll
-        for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
+          for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float w[VE];
@@ -540,17 +544,21 @@ static hipError_t launch_rows_t(const RowParams& P, const TreeDesc& td, int cfg,
   }
 }
 
-// Smallest (threads, vectors per thread) whose single tile holds the row; rows longer
-// than one 512 x 16 tile use several tiles of it.
-RowConfig choose_row_config(bool bf16, int V, int head_max) {
+// Smallest (threads, vectors per thread) whose single tile holds the row.  Rows longer than
+// one 256 x 16 tile are walked in tiles: of 256 x 16 when the batch has enough rows to give
+// every CU two workgroups (occupancy hides latency best there), of 512 x 16 when it has
+// few rows (each workgroup then keeps twice the bytes in flight).
+RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows) {
   static const int nt[kRowConfigs] = {64, 256, 256, 512};
   static const int nv[kRowConfigs] = {4, 4, 16, 16};
+  constexpr int64_t kManyRows = 512;
   const int ve = bf16 ? 8 : 4;
   const long long need = static_cast<long long>(V) + head_max;
+  const int widest = rows >= kManyRows ? kRowConfigs - 2 : kRowConfigs - 1;
   RowConfig rc{};
-  for (int i = 0; i < kRowConfigs; ++i) {
+  for (int i = 0; i <= widest; ++i) {
     const long long cap = static_cast<long long>(nt[i]) * nv[i] * ve;
-    if (cap >= need || i == kRowConfigs - 1) {
+    if (cap >= need || i == widest) {
       rc.cfg = i;
       rc.threads = nt[i];
       rc.ntiles = static_cast<int>((need + cap - 1) / cap);

@@ -54,6 +54,13 @@ def test_ragged_and_multi_tile_vocab(dtype, V):
               what=f"ragged V={V} {dtype}")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 40001), ("f32", 20001), ("bf16", 65537)])
+def test_many_rows_multi_tile(dtype, V):
+    # 512 rows: long rows are walked in 256-thread tiles instead of 512-thread ones
+    _case_run(linear_case(128, 3, V, seed=V + 7, dtype=dtype, noise_sigma=1.0), seed=6,
+              what=f"many rows V={V} {dtype}")
+
+
 @pytest.mark.parametrize("misalign", [(1, 0), (0, 1), (3, 5), (1, 1)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_misaligned_bases(dtype, misalign):
