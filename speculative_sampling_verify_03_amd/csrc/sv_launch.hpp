@@ -41,7 +41,7 @@ struct TreeDesc {
   int32_t D;  // maximum depth
 };
 
-constexpr int kRowConfigs = 4;
+constexpr int kRowConfigs = 5;
 struct RowConfig {
   int cfg;      // index into the (threads, vectors per thread) table
   int threads;

@@ -539,32 +539,37 @@ static hipError_t launch_rows_t(const RowParams& P, const TreeDesc& td, int cfg,
   switch (cfg) {
     case 0: return launch_one<BF16, 64, 4, TREE, QMODE>(P, td, grid, st);
     case 1: return launch_one<BF16, 256, 4, TREE, QMODE>(P, td, grid, st);
-    case 2: return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
+    case 2: return launch_one<BF16, 512, 8, TREE, QMODE>(P, td, grid, st);
+    case 3: return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
     default: return launch_one<BF16, 512, 16, TREE, QMODE>(P, td, grid, st);
   }
 }
 
-// Smallest (threads, vectors per thread) whose single tile holds the row.  Rows longer than
-// one 256 x 16 tile are walked in tiles: of 256 x 16 when the batch has enough rows to give
+// A row that fits 64 x 4, 256 x 4 or 512 x 8 (the first that holds it) is one tile with
+// few vectors per thread: the per-element work of both passes is then spread over more
+// waves (512 x 8 measured faster than 256 x 16 and than 1024 x 4 at V = 32000 bf16).
+// Longer rows are walked in tiles: of 256 x 16 when the batch has enough rows to give
 // every CU two workgroups (occupancy hides latency best there), of 512 x 16 when it has
 // few rows (each workgroup then keeps twice the bytes in flight).
 RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows) {
-  static const int nt[kRowConfigs] = {64, 256, 256, 512};
-  static const int nv[kRowConfigs] = {4, 4, 16, 16};
+  static const int nt[kRowConfigs] = {64, 256, 512, 256, 512};
+  static const int nv[kRowConfigs] = {4, 4, 8, 16, 16};
+  constexpr int kSingleTileConfigs = 3;
   constexpr int64_t kManyRows = 512;
   const int ve = bf16 ? 8 : 4;
   const long long need = static_cast<long long>(V) + head_max;
-  const int widest = rows >= kManyRows ? kRowConfigs - 2 : kRowConfigs - 1;
-  RowConfig rc{};
-  for (int i = 0; i <= widest; ++i) {
-    const long long cap = static_cast<long long>(nt[i]) * nv[i] * ve;
-    if (cap >= need || i == widest) {
-      rc.cfg = i;
-      rc.threads = nt[i];
-      rc.ntiles = static_cast<int>((need + cap - 1) / cap);
+  int cfg = rows >= kManyRows ? kRowConfigs - 2 : kRowConfigs - 1;
+  for (int i = 0; i < kSingleTileConfigs; ++i) {
+    if (static_cast<long long>(nt[i]) * nv[i] * ve >= need) {
+      cfg = i;
       break;
     }
   }
+  const long long cap = static_cast<long long>(nt[cfg]) * nv[cfg] * ve;
+  RowConfig rc{};
+  rc.cfg = cfg;
+  rc.threads = nt[cfg];
+  rc.ntiles = static_cast<int>((need + cap - 1) / cap);
   return rc;
 }
 

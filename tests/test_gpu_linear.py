@@ -47,6 +47,7 @@ def test_cfg3_full_stochastic():
 
 
 @pytest.mark.parametrize("dtype,V", [("f32", 1003), ("bf16", 1001), ("f32", 5), ("bf16", 1), ("bf16", 777),
+                                     ("bf16", 20001), ("f32", 10001), ("bf16", 32761),
                                      ("f32", 65537), ("bf16", 131075), ("f32", 150000), ("bf16", 200003)])
 def test_ragged_and_multi_tile_vocab(dtype, V):
     B = 24 if V > 100000 else 64
