@@ -30,15 +30,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["speculative_sampling_verify_03_amd/csrc/verify_rows.hip",
-                  "speculative_sampling_verify_03_amd/csrc/verify_greedy.hip",
-                  "speculative_sampling_verify_03_amd/csrc/lmhead_gemm.hip",
-                  "speculative_sampling_verify_03_amd/csrc/sv_device.hpp"]
+# Sources that determine each kernel family's code and launch shape.  The HBM traffic table
+# under profiles/ records the digest of the family a workload's dominant kernel belongs to;
+# a row whose digest no longer matches is stale and reported as null.
+_CSRC = "speculative_sampling_verify_03_amd/csrc/"
+KERNEL_SOURCES = {
+    "rows": [_CSRC + f for f in ("verify_rows.hip", "sv_device.hpp", "sv_launch.hpp", "api.hip")],
+    "greedy": [_CSRC + f for f in ("verify_greedy.hip", "sv_device.hpp", "sv_launch.hpp", "api.hip",
+                                   "validate.cpp")],
+    "lmhead": [_CSRC + f for f in ("lmhead_gemm.hip", "sv_device.hpp", "sv_launch.hpp")]
+              + ["speculative_sampling_verify_03_amd/build.py"],
+}
 
 
-def kernel_digest() -> str:
+def kernel_family(workload: str) -> str:
+    if workload.startswith("greedy"):
+        return "greedy"
+    if workload.startswith("lmhead"):
+        return "lmhead"
+    return "rows"
+
+
+def kernel_digest(family: str = "rows") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -321,10 +336,10 @@ def traffic_for(name):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    digest = kernel_digest()
+    digest = kernel_digest(kernel_family(name))
     for line in open(path):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 5 and cells[0] == name and cells[1] == digest:
+        if len(cells) >= 5 and cells[0] == name and cells[1] == digest:
             try:
                 return int(cells[4])
             except ValueError:
@@ -434,7 +449,7 @@ def main():
         "hbm_gbs": roofline["achieved"],
         "hbm_frac": roofline["frac"],
         "resident_input_bytes": int(wl.resident_bytes),
-        "kernel_digest": kernel_digest(),
+        "kernel_digest": kernel_digest(kernel_family(wl.name)),
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
