@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--workload", default="linear-b64-k5-v32000",
                     choices=["linear-b64-k5-v32000", "linear-b1-k4-v1024", "linear-b1000-k4-v1024",
                              "linear-b256-k8-v128256", "greedy-b256-k8-v128256", "tree-b16-n61-v128256",
-                             "lmhead-b32-k5-h8192-v128256", "copy-probe"])
+                             "lmhead-b32-k5-h8192-v128256", "linear-b256-k1-v128256", "linear-plug-b64-k5-v32000",
+                             "copy-probe"])
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -150,6 +151,25 @@ class Linear:
             if el >= budget_s:
                 break
         return done * self.k / el, f"{done} sequences of the first input batch ({done * self.k} positions), one at a time"
+
+
+class LinearPlug(Linear):
+    """Linear verification followed by the on-device token plug of its outputs (the next
+    step's inputs are set up without reading accept_len back to the host)."""
+
+    def setup(self, sv, torch, rotate_bytes):
+        super().setup(sv, torch, rotate_bytes)
+        self.cap = 16384
+        self.seq_len = torch.zeros(self.B, dtype=torch.int32, device="cuda")
+        self.history = torch.zeros((self.B, self.cap), dtype=torch.int32, device="cuda")
+        self.next_token = torch.zeros(self.B, dtype=torch.int32, device="cuda")
+
+    def launch(self, i):
+        super().launch(i)
+        self.sv.spec_plug_tokens(self.tokens, self.alen, self.seq_len, self.history, self.next_token)
+
+    def launch_verify_only(self, i):
+        super().launch(i)
 
 
 class Greedy(Linear):
@@ -312,7 +332,7 @@ class LMHead:
 
 
 def make_workload(name):
-    from synthetic import cfg1_case, cfg2_case, cfg3_case
+    from synthetic import cfg1_case, cfg2_case, cfg3_case, mtp_case
     if name == "linear-b64-k5-v32000":
         return Linear(name, lambda s: cfg2_case(seed=s), [2, 102, 202, 302], "bf16", 1.0)
     if name == "linear-b1-k4-v1024":
@@ -321,6 +341,10 @@ def make_workload(name):
         return Linear(name, lambda s: cfg1_case(B=1000, seed=s), [1, 101], "f32", 1.0)
     if name == "linear-b256-k8-v128256":
         return Linear(name, lambda s: cfg3_case(seed=s), [3], "bf16", 0.7)
+    if name == "linear-b256-k1-v128256":  # single-token MTP regime: 2 rows per sequence
+        return Linear(name, lambda s: mtp_case(seed=s), [6, 106], "bf16", 1.0)
+    if name == "linear-plug-b64-k5-v32000":
+        return LinearPlug(name, lambda s: cfg2_case(seed=s), [2, 102, 202, 302], "bf16", 1.0)
     if name == "greedy-b256-k8-v128256":
         return Greedy(name, lambda s: cfg3_case(seed=s), [3], "bf16", 0.7)
     if name == "tree-b16-n61-v128256":
@@ -389,6 +413,18 @@ def main():
     ms_step = ms_total / args.steps
 
     extra = {}
+    if isinstance(wl, LinearPlug):
+        # the plug's own cost: the step minus verification alone
+        torch.cuda.synchronize()
+        s2 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        s2.record(stream)
+        for i in range(args.steps):
+            wl.launch_verify_only(i)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        extra["verify_ms"] = round(s2.elapsed_time(e2) / args.steps, 5)
+        extra["plug_ms"] = round(ms_step - extra["verify_ms"], 5)
     if isinstance(wl, LMHead):
         # the GEMM dominates: its time is the step minus the verification-only time
         torch.cuda.synchronize()
@@ -409,12 +445,13 @@ def main():
                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
         extra["verify_ms"] = round(ms_verify, 4)
     else:
-        achieved = wl.algorithmic_bytes() / (ms_step * 1e-3) / 1e9
+        kernel_ms = extra.get("verify_ms", ms_step)  # with the plug: the verification kernel alone
+        achieved = wl.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
         kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)"}.get(type(wl).__name__,
                                                                                    "row_verify_kernel(linear)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
-                    "kernel": kname, "kernel_ms": round(ms_step, 5),
+                    "kernel": kname, "kernel_ms": round(kernel_ms, 5),
                     "algorithmic_bytes_per_launch": int(wl.algorithmic_bytes())}
 
     value = wl.positions() / (ms_step * 1e-3)

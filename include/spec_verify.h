@@ -157,6 +157,30 @@ SV_API int spec_lmhead_verify(const void* hidden, const void* lm_head,
                        float* out_target_prob, float* out_accept_prob,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * On-device token plug ("Accelerating Sonar through speculation", section "MTP schedule for
+ * one token": after the target's input tokens are shifted, a kernel plugs the next tokens
+ * into their positions, so the accepted lengths need no GPU-to-CPU read before the next
+ * step is set up).  Reads the outputs of a verify call and, for every sequence b with
+ * n = out_accept_len[b]:
+ *   history[b, seq_len[b] + i] = out_tokens[b, i]   for i = 0..n (positions >= cap dropped)
+ *   next_token[b] = out_tokens[b, n]                (the input of the next draft step)
+ *   seq_len[b]    = min(seq_len[b] + n + 1, cap)
+ *   status[b]     = 0, or 1 when tokens were dropped at cap, or 2 when n is not in
+ *                   [0, W-1] or seq_len[b] is not in [0, cap] (nothing is written then).
+ *
+ *   out_tokens     [B, W] int32   as written by a verify call (W = k+1; tree: D+1)
+ *   out_accept_len [B] int32
+ *   seq_len        [B] int32      in/out
+ *   history        [B, cap] int32 in/out (row-major, one row of capacity cap per sequence)
+ *   next_token     [B] int32 or NULL
+ *   status         [B] int32 or NULL
+ * Needs no workspace.  W must be in [1, 64], cap >= 1.
+ */
+SV_API int spec_plug_tokens(const int32_t* out_tokens, const int32_t* out_accept_len, int32_t B, int32_t W,
+                     int32_t* seq_len, int32_t* history, int32_t cap, int32_t* next_token, int32_t* status,
+                     void* stream);
+
 /* Workspace bytes for a call of `kind` (SV_KIND_*) with the given sizes (k_or_N = k for
  * linear / greedy / lmhead, N for tree; H is used by lmhead only).  Returns 0 for invalid
  * arguments. */

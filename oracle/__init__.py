@@ -18,7 +18,9 @@ layout, tie rules, the tree's bonus rule) are stated next to the code that takes
 Pinned by tests/test_oracle_*.py against: numpy's independent Philox4x64-10, exact
 rational enumeration on tiny vocabularies, chi-square tests of the emitted-token law,
 the closed form for the mean emitted length under i.i.d. acceptance, the greedy
-identity, the worst and best cases the pages state, and scipy's softmax.
+identity, the worst and best cases the pages state, and scipy's softmax.  The token plug
+is pinned by its invariants (length arithmetic, untouched prefixes, capacity) and by a
+multi-step run whose history must equal the concatenated outputs.
 """
 from .philox import philox4x64_10, uniforms  # noqa: F401
 from .verify import (  # noqa: F401
@@ -32,3 +34,4 @@ from .verify import (  # noqa: F401
     lmhead_gemm_error_bound,
     verify_lmhead,
 )
+from .plug import plug_tokens  # noqa: F401

@@ -24,7 +24,7 @@ ERRORS = {
     -5: "SV_E_TREE", -6: "SV_E_WORKSPACE", -7: "SV_E_DEVICE", -8: "SV_E_LAUNCH", -9: "SV_E_ALIGN",
 }
 EXPORTS = ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
-           "spec_verify_workspace_bytes", "spec_verify_strerror")
+           "spec_plug_tokens", "spec_verify_workspace_bytes", "spec_verify_strerror")
 
 
 class SpecVerifyError(RuntimeError):
@@ -55,7 +55,9 @@ def _lib():
                                          _U64, _U64, _P, _P, _P, _P, _SZ, _P]
         lib.spec_lmhead_verify.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _F32,
                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]
-        for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify"):
+        lib.spec_plug_tokens.argtypes = [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
+        for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
+                   "spec_plug_tokens"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.spec_verify_workspace_bytes.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32]
         lib.spec_verify_workspace_bytes.restype = _SZ
@@ -158,6 +160,18 @@ def spec_verify_greedy(target_logits, draft_tokens, out_tokens, out_accept_len, 
         _i32(out_tokens, (B, R), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_verify_greedy")
+
+
+def spec_plug_tokens(out_tokens, out_accept_len, seq_len, history, next_token=None, status=None, stream=None):
+    """out_tokens int32 [B, W], out_accept_len [B] (a verify call's outputs); seq_len int32
+    [B] and history int32 [B, cap] are updated in place; next_token / status int32 [B]."""
+    B, W = out_tokens.shape
+    cap = history.shape[1] if history.dim() == 2 else 0
+    rc = _lib().spec_plug_tokens(
+        _i32(out_tokens, (B, W), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"), B, W,
+        _i32(seq_len, (B,), "seq_len"), _i32(history, (B, cap), "history"), cap,
+        _i32(next_token, (B,), "next_token"), _i32(status, (B,), "status"), _stream(stream))
+    _check(rc, "spec_plug_tokens")
 
 
 def spec_verify_tree(target_logits, draft_probs, node_tokens, parents, temperature, seed, offset,

@@ -189,4 +189,24 @@ const char* spec_verify_strerror(int code) {
   }
 }
 
+int spec_plug_tokens(const int32_t* out_tokens, const int32_t* out_accept_len, int32_t B, int32_t W,
+                     int32_t* seq_len, int32_t* history, int32_t cap, int32_t* next_token, int32_t* status,
+                     void* stream) {
+  int rc = sv::validate_plug(out_tokens, out_accept_len, B, W, seq_len, history, cap, next_token, status);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  sv::PlugParams P{};
+  P.tokens = out_tokens;
+  P.accept_len = out_accept_len;
+  P.seq_len = seq_len;
+  P.history = history;
+  P.next_token = next_token;
+  P.status = status;
+  P.B = B;
+  P.W = W;
+  P.cap = cap;
+  (void)hipGetLastError();
+  return sv::launch_plug(P, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_E_LAUNCH;
+}
+
 }  // extern "C"

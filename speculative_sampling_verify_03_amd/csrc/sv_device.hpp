@@ -60,6 +60,20 @@ __device__ __forceinline__ Vec16 ld16(const SV_GLOBAL Vec16* p, int i, int n) {
   return v;
 }
 
+// 16-byte load of vector i when 0 <= i < n, else of vector 0 (n >= 1), with no select on the
+// result: for logits rows, mask_edges below turns every element of a vector past the row
+// into -inf anyway.  Loads with no consumer inside a conditional block (the next tile's
+// prefetch) then carry no wait with them.
+__device__ __forceinline__ Vec16 ld16_any(const SV_GLOBAL Vec16* p, int i, int n) {
+  const SV_GLOBAL Vec16& g = p[static_cast<unsigned>(i) < static_cast<unsigned>(n) ? i : 0];
+  Vec16 v;
+  v.w[0] = g.w[0];
+  v.w[1] = g.w[1];
+  v.w[2] = g.w[2];
+  v.w[3] = g.w[3];
+  return v;
+}
+
 // Elements of a vector that fall outside [0, V) (e0 = token id of element 0) are set to
 // -inf: they then drop out of every max, exp-sum, residual and argmax without per-element
 // bounds tests in the hot loops.  Only the first and last vector of a row can be partial.

@@ -71,4 +71,17 @@ hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t st);
 hipError_t launch_lmhead_gemm(const void* hidden, const void* w, float* logits, int M, int H, int V,
                               hipStream_t st);
 
+// Token plug: one wave per sequence.
+struct PlugParams {
+  const int32_t* tokens;      // [B, W]
+  const int32_t* accept_len;  // [B]
+  int32_t* seq_len;           // [B] in/out
+  int32_t* history;           // [B, cap] in/out
+  int32_t* next_token;        // [B] or null
+  int32_t* status;            // [B] or null
+  int64_t B;
+  int32_t W, cap;
+};
+hipError_t launch_plug(const PlugParams& P, hipStream_t st);
+
 }  // namespace sv

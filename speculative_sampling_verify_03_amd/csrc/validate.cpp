@@ -166,4 +166,16 @@ int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt
   return check_ws(ws, ws_bytes, SV_KIND_LMHEAD, B, k, V, H);
 }
 
+int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, int32_t W, const int32_t* seq_len,
+                  const int32_t* history, int32_t cap, const int32_t* next_token, const int32_t* status) {
+  if (B < 0 || W < 1 || W > kMaxRows || cap < 1) return SV_E_SHAPE;
+  if (!mul_ok(B, W, int64_t(1) << 40) || !mul_ok(B, cap, int64_t(1) << 50)) return SV_E_SHAPE;
+  if (B == 0) return SV_OK;
+  if (!tokens || !accept_len || !seq_len || !history) return SV_E_NULL;
+  const void* ptrs[6] = {tokens, accept_len, seq_len, history, next_token, status};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 3) return SV_E_ALIGN;
+  return SV_OK;
+}
+
 }  // namespace sv

@@ -51,4 +51,7 @@ int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt
                     int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
                     const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes);
 
+int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, int32_t W, const int32_t* seq_len,
+                  const int32_t* history, int32_t cap, const int32_t* next_token, const int32_t* status);
+
 }  // namespace sv

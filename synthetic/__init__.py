@@ -16,6 +16,7 @@ from .generators import (  # noqa: F401
     cfg3_case,
     cfg4_case,
     cfg5_case,
+    mtp_case,
     tree_case,
     lmhead_case,
     eagle_tree_parents,

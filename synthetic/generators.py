@@ -161,6 +161,14 @@ def cfg3_case(seed: int = 3, B: int = 256) -> Case:
                        noise_sigma=0.5, temperature=0.7)
 
 
+def mtp_case(seed: int = 6, B: int = 256) -> Case:
+    """Single-token MTP regime of "Accelerating Sonar through speculation" (section "MTP
+    schedule for one token": one drafted token per sequence, the target checks 2 tokens per
+    sequence): B=256, k=1, V=128256, bf16, T=1, cfg1-style logits."""
+    return linear_case(B, 1, 128256, seed=seed, dtype="bf16", draft_sigma=2.0, noise_sigma=0.5,
+                       temperature=1.0)
+
+
 def eagle_tree_parents(branching=(4, 2, 2, 2), max_nodes: int = 61) -> np.ndarray:
     """Parent array of a static tree in BFS order: the root has branching[0] children,
     every node of level d has branching[d] children, truncated to ``max_nodes`` slots

@@ -152,3 +152,21 @@ def test_lmhead_validation_codes():
     assert lmhead(qt=5) == -3
     assert lmhead(T=0.0) == -4
     assert lmhead(B=0) == 0
+
+
+def plug(**kw):
+    a = dict(toks=FAKE, alen=FAKE, B=2, W=6, seq=FAKE, hist=FAKE, cap=100, nxt=None, status=None, stream=None)
+    a.update(kw)
+    return sv.library().spec_plug_tokens(*a.values())
+
+
+def test_plug_validation_codes():
+    assert plug(B=0) == 0
+    assert plug(toks=None) == -1
+    assert plug(hist=None) == -1
+    assert plug(seq=None) == -1
+    assert plug(W=0) == -2
+    assert plug(W=65) == -2
+    assert plug(cap=0) == -2
+    assert plug(B=-1) == -2
+    assert plug(nxt=C(0x1002)) == -9      # int32 outputs must be 4-byte aligned

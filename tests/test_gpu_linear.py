@@ -6,7 +6,7 @@ import torch
 from scipy import stats
 
 from gpu_common import announce, check_linear, oracle_linear, run_linear
-from synthetic import cfg1_case, cfg2_case, cfg3_case, fixed_pq_case, linear_case, to_numpy_f64
+from synthetic import cfg1_case, cfg2_case, cfg3_case, fixed_pq_case, linear_case, mtp_case, to_numpy_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,11 @@ def test_cfg2_full():
 
 def test_cfg3_full_stochastic():
     got, ref = _case_run(cfg3_case(), seed=0, what="B=256 k=8 V=128256 bf16 T=0.7")
+
+
+def test_mtp_single_token_regime():
+    # one drafted token per sequence, 256 sequences, Llama-3 vocabulary
+    _case_run(mtp_case(), seed=0, what="B=256 k=1 V=128256 bf16 (MTP regime)")
 
 
 @pytest.mark.parametrize("dtype,V", [("f32", 1003), ("bf16", 1001), ("f32", 5), ("bf16", 1), ("bf16", 777),
