@@ -18,10 +18,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b
 }  // namespace
 
 int greedy_splits(int32_t B, int32_t R, int32_t V) {
+  // About 8192 workgroups (four rounds of the 2048 that fit the chip at once), so the last
+  // round is a small share of the time; at most one split per 16K vocabulary entries, since
+  // every split adds two device-scope atomics on the row's words (B=256, k=8, V=128256:
+  // 4 splits measured 128 us against 134 us for 1, 149 us for 8 and 255 us for 16).
   const int64_t rows = static_cast<int64_t>(B) * R;
   if (rows <= 0) return 1;
-  int64_t want = (2048 + rows - 1) / rows;
-  int64_t cap = V / 4096;
+  int64_t want = (8192 + rows - 1) / rows;
+  int64_t cap = V / 16384;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
   if (want > 64) want = 64;

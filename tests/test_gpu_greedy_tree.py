@@ -35,6 +35,19 @@ def test_greedy_ragged(dtype, V, misalign):
     check_greedy(got, case.logits, case.greedy_tokens, what=f"greedy V={V} {dtype} misalign={misalign}")
 
 
+def test_greedy_ties_across_splits():
+    # V = 65536 with 32 rows: each row is split over 4 workgroups; equal maxima sit in
+    # different splits and the lowest index must win the cross-workgroup merge
+    V = 65536
+    L = torch.zeros((8, 4, V), dtype=torch.bfloat16)
+    L[:, :, [20000, 17, 40000, 65535]] = 3.0
+    X = torch.tensor([[17, 17, 17], [20000, 17, 17], [17, 40000, 17], [17, 17, 65535]] * 2, dtype=torch.int32)
+    got = run_greedy(L, X)
+    assert list(got["accept_len"][:4]) == [3, 0, 1, 2]
+    assert np.all(got["tokens"][:, 0] == 17)
+    check_greedy(got, L, X, what="greedy ties across splits")
+
+
 def test_greedy_ties_lowest_index():
     V = 4096
     L = torch.zeros((8, 4, V), dtype=torch.bfloat16)
