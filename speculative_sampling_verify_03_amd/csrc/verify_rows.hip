@@ -275,28 +275,32 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         w[e] = x;
       }
     };
-    auto reload = [&](int v0) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) buf[i] = ld16_any(vrow, v0 + i * kWave, nvec);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
-    };
-    // Per-vector sums of this thread's share of a tile (seg[]), each slot's total over the
-    // wave (slot_tot[], the last lane of the slot's scan) and the wave's total (their
-    // sequential sum).  The search below walks exactly these sums, so every level of the
-    // inverse CDF agrees with the level above it.  q loads go out together while
-    // registers allow (one round trip).
+    // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total.  With
+    // `slots`, also each slot's total over the wave (slot_tot[], the last lane of the slot's
+    // scan), the wave's total being their sequential sum: the search below walks exactly
+    // these sums, so every level of the inverse CDF agrees with the level above it.  Tiles
+    // whose totals only enter the unit weights skip the per-slot scans.  A tile that is not
+    // in registers (`reload_row`) is re-read together with its first batch of q vectors, so
+    // the two reads share one round trip.
     float seg[NV];
     float slot_tot[NV];
-    auto tile_totals = [&](int v0) -> float {
+    auto tile_totals = [&](int v0, bool reload_row, bool slots) -> float {
       constexpr int GQ = QMODE == kQElem ? 2 : (NT >= 512 && QMODE == kQVec) ? 8 : NV;
       constexpr int G = NV < GQ ? NV : GQ;
+      if (reload_row) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) buf[i] = ld16_any(vrow, v0 + i * kWave, nvec);
+      }
 #pragma unroll
       for (int g0 = 0; g0 < NV; g0 += G) {
         Vec16 qv[G] = {};
         if (resid) {  // one uniform branch around the whole batch of q loads
 #pragma unroll
           for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
+        }
+        if (g0 == 0 && reload_row) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -309,10 +313,17 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
       }
       float wt = 0.f;
+      if (slots) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        slot_tot[i] = lane_value(wave_inclusive_scan(seg[i]), 63);
-        wt += slot_tot[i];
+        for (int i = 0; i < NV; ++i) {
+          slot_tot[i] = lane_value(wave_inclusive_scan(seg[i]), 63);
+          wt += slot_tot[i];
+        }
+      } else {
+        float own = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) own += seg[i];
+        wt = wave_sum(own);
       }
       return wt;
     };
@@ -373,11 +384,10 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
         if (active) {
           const int v0 = tile * TILE + wid * (NV * kWave) + lane;
-          if (tile != loaded_tile) {  // only this wave's share when locating the winner
-            reload(v0);
-            loaded_tile = tile;
-          }
-          const float wt = tile_totals(v0);
+          const bool reload_row = tile != loaded_tile;  // only this wave's share when locating the winner
+          loaded_tile = tile;
+          // slot totals for the tile that stays in registers (the last step) and for the winner
+          const float wt = tile_totals(v0, reload_row, step >= P.ntiles - 1);
           if (step < P.ntiles && lane == 0) s_tot[tile * NW + wid] = wt;
         }
       }
