@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
                                    "validate.cpp")],
     "lmhead": [_CSRC + f for f in ("lmhead_gemm.hip", "sv_device.hpp", "sv_launch.hpp")]
               + ["speculative_sampling_verify_03_amd/build.py"],
+    "lookup": [_CSRC + f for f in ("lookup.hip", "sv_device.hpp", "sv_launch.hpp")],
 }
 
 
@@ -48,6 +49,8 @@ def kernel_family(workload: str) -> str:
         return "greedy"
     if workload.startswith("lmhead"):
         return "lmhead"
+    if workload.startswith("lookup"):
+        return "lookup"
     return "rows"
 
 
@@ -68,7 +71,7 @@ def parse():
                     choices=["linear-b64-k5-v32000", "linear-b1-k4-v1024", "linear-b1000-k4-v1024",
                              "linear-b256-k8-v128256", "greedy-b256-k8-v128256", "tree-b16-n61-v128256",
                              "lmhead-b32-k5-h8192-v128256", "linear-b256-k1-v128256", "linear-plug-b64-k5-v32000",
-                             "copy-probe"])
+                             "lookup-b64-l8192-n3-k5", "copy-probe"])
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -331,6 +334,74 @@ class LMHead:
         return done * self.k / el, f"{done} sequence(s) of 6 rows, float64 GEMM + verification"
 
 
+class Lookup:
+    """Prompt-lookup drafting over token histories that echo their own prompt (a document
+    followed by a response that copies spans of it), B sequences of up to `cap` tokens,
+    phrase lengths min_ngram..max_ngram, k drafts per sequence."""
+    metric = "proposed draft positions/sec"
+
+    def __init__(self, name, B, cap, min_ngram, max_ngram, k, seeds):
+        self.name, self.B, self.cap = name, B, cap
+        self.mn, self.mx, self.k = min_ngram, max_ngram, k
+        self.seeds = seeds
+
+    def setup(self, sv, torch, rotate_bytes):
+        from synthetic import lookup_histories
+        self.sv, self.torch = sv, torch
+        self.cases = [lookup_histories(self.B, self.cap, seed=s) for s in self.seeds]
+        per_set = self.B * self.cap * 4
+        nsets = max(len(self.cases), int(np.ceil(rotate_bytes / per_set)))
+        self.sets = []
+        for i in range(nsets):
+            h, L = self.cases[i % len(self.cases)]
+            self.sets.append((torch.as_tensor(h, dtype=torch.int32).cuda(),
+                              torch.as_tensor(L, dtype=torch.int32).cuda()))
+        self.drafts = torch.empty((self.B, self.k), dtype=torch.int32, device="cuda")
+        self.count = torch.empty((self.B,), dtype=torch.int32, device="cuda")
+        self.resident_bytes = per_set * nsets
+
+    def launch(self, i):
+        h, L = self.sets[i % len(self.sets)]
+        self.sv.spec_lookup_drafts(h, L, self.mn, self.mx, self.drafts, self.count)
+
+    def positions(self):
+        return self.B * self.k
+
+    def _extent(self, h, length):
+        """Tokens a scan must read: up to the end of the longest phrase's earliest earlier
+        occurrence when there is one (it decides and ends the scan), else the whole history."""
+        if length - 1 < self.mx:
+            return length
+        from numpy.lib.stride_tricks import sliding_window_view
+        win = sliding_window_view(h[:length - 1], self.mx)
+        hit = np.flatnonzero((win == h[length - self.mx:length]).all(axis=1))
+        return int(hit[0]) + self.mx if hit.size else length
+
+    def algorithmic_bytes(self):
+        tot = 0.0
+        for h, L in self.cases:
+            tot += sum(self._extent(h[b], int(L[b])) for b in range(self.B)) * 4
+        return tot / len(self.cases) + self.B * 4 + self.B * (self.k + 1) * 4
+
+    def config(self):
+        return {"workload": self.name, "batch": self.B, "history_cap": self.cap, "min_ngram": self.mn,
+                "max_ngram": self.mx, "draft_len": self.k}
+
+    def oracle_sample(self, budget_s):
+        from oracle import lookup_drafts
+        h, L = self.cases[0]
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            b = done % self.B
+            lookup_drafts(h[b:b + 1], L[b:b + 1], self.mn, self.mx, self.k)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        return done * self.k / el, f"{done} sequences of the first history batch, one at a time"
+
+
 def make_workload(name):
     from synthetic import cfg1_case, cfg2_case, cfg3_case, mtp_case
     if name == "linear-b64-k5-v32000":
@@ -351,6 +422,8 @@ def make_workload(name):
         return Tree(name, [5, 105])
     if name == "lmhead-b32-k5-h8192-v128256":
         return LMHead()
+    if name == "lookup-b64-l8192-n3-k5":
+        return Lookup(name, 64, 8192, 1, 3, 5, [7, 107])
     raise ValueError(name)
 
 
@@ -447,7 +520,7 @@ def main():
     else:
         kernel_ms = extra.get("verify_ms", ms_step)  # with the plug: the verification kernel alone
         achieved = wl.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
-        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)"}.get(type(wl).__name__,
+        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel"}.get(type(wl).__name__,
                                                                                    "row_verify_kernel(linear)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
@@ -463,10 +536,10 @@ def main():
                 cpu_value, sample = wl.oracle_sample(args.cpu_seconds)
         except ImportError:
             cpu_value, sample = wl.oracle_sample(args.cpu_seconds)
-        cpu = {"value": round(cpu_value, 2), "unit": "verified draft positions/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(cpu_value, 2), "unit": getattr(wl, "metric", "verified draft positions/sec").replace("/sec", "/s"), "cores": 1, "kind": "oracle",
                "sample": sample}
     line = {
-        "metric": "verified draft positions/sec",
+        "metric": getattr(wl, "metric", "verified draft positions/sec"),
         "value": round(value, 1),
         "unit": "positions/s",
         "n_gpus": 1,
@@ -478,7 +551,7 @@ def main():
         "vs_baseline": None,
         # arithmetic type: the verification kernels compute in float32 whatever the input
         # dtype; the LM-head GEMM multiplies bf16 on the matrix cores (fp32 accumulation)
-        "dtype": "bf16" if isinstance(wl, LMHead) else "f32",
+        "dtype": "bf16" if isinstance(wl, LMHead) else "int32" if isinstance(wl, Lookup) else "f32",
         "data": "synthetic",
         "config": wl.config(),
         "roofline": roofline,

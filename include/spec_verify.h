@@ -181,6 +181,24 @@ SV_API int spec_plug_tokens(const int32_t* out_tokens, const int32_t* out_accept
                      int32_t* seq_len, int32_t* history, int32_t cap, int32_t* next_token, int32_t* status,
                      void* stream);
 
+/*
+ * Prompt-lookup drafting ("Speculative decoding explained", section "Variants without a
+ * separate draft model": with no draft model, drafts are phrases found again in the prompt
+ * and history).  For each sequence b with history h = history[b, 0..len), len = seq_len[b]:
+ * for n = max_ngram down to min_ngram, the phrase h[len-n .. len) is looked up at the
+ * earliest start i with i + n < len and h[i .. i+n) equal to it; the first n that matches
+ * gives out_drafts[b] = h[i+n .. min(i+n+k, len)) padded with -1 and out_count[b] = their
+ * number.  No match (or len outside [0, cap]) gives out_count[b] = 0 and all -1.  The drafts
+ * can be verified as one-hot draft distributions or greedily.
+ *
+ *   history    [B, cap] int32      seq_len [B] int32
+ *   out_drafts [B, k] int32        out_count [B] int32
+ * 1 <= min_ngram <= max_ngram <= 16, 1 <= k <= 64, cap >= 1.  Needs no workspace.
+ */
+SV_API int spec_lookup_drafts(const int32_t* history, const int32_t* seq_len, int32_t B, int32_t cap,
+                       int32_t min_ngram, int32_t max_ngram, int32_t k, int32_t* out_drafts,
+                       int32_t* out_count, void* stream);
+
 /* Workspace bytes for a call of `kind` (SV_KIND_*) with the given sizes (k_or_N = k for
  * linear / greedy / lmhead, N for tree; H is used by lmhead only).  Returns 0 for invalid
  * arguments. */

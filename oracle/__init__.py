@@ -20,7 +20,8 @@ rational enumeration on tiny vocabularies, chi-square tests of the emitted-token
 the closed form for the mean emitted length under i.i.d. acceptance, the greedy
 identity, the worst and best cases the pages state, and scipy's softmax.  The token plug
 is pinned by its invariants (length arithmetic, untouched prefixes, capacity) and by a
-multi-step run whose history must equal the concatenated outputs.
+multi-step run whose history must equal the concatenated outputs; prompt lookup by
+hand-worked histories and by a search with Python's own substring find.
 """
 from .philox import philox4x64_10, uniforms  # noqa: F401
 from .verify import (  # noqa: F401
@@ -35,3 +36,4 @@ from .verify import (  # noqa: F401
     verify_lmhead,
 )
 from .plug import plug_tokens  # noqa: F401
+from .lookup import lookup_drafts  # noqa: F401

@@ -1,6 +1,7 @@
 """MI355X (gfx950) speculative verification library: linear speculative sampling, greedy
 and static-tree verification, and an LM-head projection feeding verification, behind a
-small C ABI (include/spec_verify.h), plus an on-device token plug for the next step.  This package is the thin Python binding over it."""
+small C ABI (include/spec_verify.h), plus an on-device token plug for the next step and
+prompt-lookup drafting.  This package is the thin Python binding over it."""
 from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
@@ -14,6 +15,7 @@ from ._lib import (  # noqa: F401
     library,
     new_workspace,
     spec_lmhead_verify,
+    spec_lookup_drafts,
     spec_plug_tokens,
     spec_verify_greedy,
     spec_verify_linear,

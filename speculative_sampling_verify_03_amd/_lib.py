@@ -24,7 +24,7 @@ ERRORS = {
     -5: "SV_E_TREE", -6: "SV_E_WORKSPACE", -7: "SV_E_DEVICE", -8: "SV_E_LAUNCH", -9: "SV_E_ALIGN",
 }
 EXPORTS = ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
-           "spec_plug_tokens", "spec_verify_workspace_bytes", "spec_verify_strerror")
+           "spec_plug_tokens", "spec_lookup_drafts", "spec_verify_workspace_bytes", "spec_verify_strerror")
 
 
 class SpecVerifyError(RuntimeError):
@@ -56,8 +56,9 @@ def _lib():
         lib.spec_lmhead_verify.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _F32,
                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]
         lib.spec_plug_tokens.argtypes = [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
+        lib.spec_lookup_drafts.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
         for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
-                   "spec_plug_tokens"):
+                   "spec_plug_tokens", "spec_lookup_drafts"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.spec_verify_workspace_bytes.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32]
         lib.spec_verify_workspace_bytes.restype = _SZ
@@ -172,6 +173,17 @@ def spec_plug_tokens(out_tokens, out_accept_len, seq_len, history, next_token=No
         _i32(seq_len, (B,), "seq_len"), _i32(history, (B, cap), "history"), cap,
         _i32(next_token, (B,), "next_token"), _i32(status, (B,), "status"), _stream(stream))
     _check(rc, "spec_plug_tokens")
+
+
+def spec_lookup_drafts(history, seq_len, min_ngram, max_ngram, out_drafts, out_count, stream=None):
+    """history int32 [B, cap], seq_len int32 [B]; out_drafts int32 [B, k], out_count [B]."""
+    B, cap = history.shape
+    k = out_drafts.shape[1]
+    rc = _lib().spec_lookup_drafts(
+        _i32(history, (B, cap), "history"), _i32(seq_len, (B,), "seq_len"), B, cap, int(min_ngram),
+        int(max_ngram), k, _i32(out_drafts, (B, k), "out_drafts"), _i32(out_count, (B,), "out_count"),
+        _stream(stream))
+    _check(rc, "spec_lookup_drafts")
 
 
 def spec_verify_tree(target_logits, draft_probs, node_tokens, parents, temperature, seed, offset,

@@ -209,4 +209,23 @@ int spec_plug_tokens(const int32_t* out_tokens, const int32_t* out_accept_len, i
   return sv::launch_plug(P, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_E_LAUNCH;
 }
 
+int spec_lookup_drafts(const int32_t* history, const int32_t* seq_len, int32_t B, int32_t cap, int32_t min_ngram,
+                       int32_t max_ngram, int32_t k, int32_t* out_drafts, int32_t* out_count, void* stream) {
+  int rc = sv::validate_lookup(history, seq_len, B, cap, min_ngram, max_ngram, k, out_drafts, out_count);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  sv::LookupParams P{};
+  P.history = history;
+  P.seq_len = seq_len;
+  P.B = B;
+  P.cap = cap;
+  P.min_ngram = min_ngram;
+  P.max_ngram = max_ngram;
+  P.k = k;
+  P.drafts = out_drafts;
+  P.count = out_count;
+  (void)hipGetLastError();
+  return sv::launch_lookup(P, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_E_LAUNCH;
+}
+
 }  // extern "C"

@@ -84,4 +84,16 @@ struct PlugParams {
 };
 hipError_t launch_plug(const PlugParams& P, hipStream_t st);
 
+// Prompt lookup: one workgroup per sequence.
+constexpr int kMaxNgram = 16;
+struct LookupParams {
+  const int32_t* history;  // [B, cap]
+  const int32_t* seq_len;  // [B]
+  int64_t B;
+  int32_t cap, min_ngram, max_ngram, k;
+  int32_t* drafts;         // [B, k]
+  int32_t* count;          // [B]
+};
+hipError_t launch_lookup(const LookupParams& P, hipStream_t st);
+
 }  // namespace sv

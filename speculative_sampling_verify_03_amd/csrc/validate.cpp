@@ -182,4 +182,18 @@ int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, i
   return SV_OK;
 }
 
+int validate_lookup(const int32_t* history, const int32_t* seq_len, int32_t B, int32_t cap, int32_t min_ngram,
+                    int32_t max_ngram, int32_t k, const int32_t* drafts, const int32_t* count) {
+  constexpr int kMaxNgramArg = 16;  // the kernel holds the phrase in registers
+  if (B < 0 || cap < 1 || k < 1 || k > kMaxRows) return SV_E_SHAPE;
+  if (min_ngram < 1 || max_ngram < min_ngram || max_ngram > kMaxNgramArg) return SV_E_SHAPE;
+  if (!mul_ok(B, cap, int64_t(1) << 50) || B > (int64_t(1) << 31) - 1) return SV_E_SHAPE;
+  if (B == 0) return SV_OK;
+  if (!history || !seq_len || !drafts || !count) return SV_E_NULL;
+  const void* ptrs[4] = {history, seq_len, drafts, count};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 3) return SV_E_ALIGN;
+  return SV_OK;
+}
+
 }  // namespace sv

@@ -54,4 +54,7 @@ int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt
 int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, int32_t W, const int32_t* seq_len,
                   const int32_t* history, int32_t cap, const int32_t* next_token, const int32_t* status);
 
+int validate_lookup(const int32_t* history, const int32_t* seq_len, int32_t B, int32_t cap, int32_t min_ngram,
+                    int32_t max_ngram, int32_t k, const int32_t* drafts, const int32_t* count);
+
 }  // namespace sv

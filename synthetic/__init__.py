@@ -17,6 +17,7 @@ from .generators import (  # noqa: F401
     cfg4_case,
     cfg5_case,
     mtp_case,
+    lookup_histories,
     tree_case,
     lmhead_case,
     eagle_tree_parents,

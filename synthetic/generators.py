@@ -295,3 +295,28 @@ def fixed_pq_case(p: np.ndarray, q: np.ndarray, B: int, *, seed: int,
     return Case(logits=logits, draft_probs=probs, draft_tokens=torch.from_numpy(toks),
                 greedy_tokens=torch.from_numpy(greedy), temperature=1.0,
                 meta=dict(seed=seed, dtype=dtype))
+
+
+def lookup_histories(B: int, cap: int, vocab: int = 32000, seed: int = 0, doc_frac: float = 0.7):
+    """Token histories for prompt lookup, standing in for the page's code-editing and
+    summarisation prompts: a random "document" of about doc_frac * cap tokens, then a
+    "response" that copies spans of 4-32 tokens from it with one token in ten replaced at
+    random.  Lengths vary between cap/2 and cap.  Returns (history int64 [B, cap] with -1
+    past each length, lengths int64 [B])."""
+    rng = np.random.default_rng(seed)
+    hist = np.full((B, cap), -1, dtype=np.int64)
+    lens = rng.integers(max(1, cap // 2), cap + 1, size=B)
+    for b in range(B):
+        L = int(lens[b])
+        nd = max(1, int(L * doc_frac))
+        doc = rng.integers(0, vocab, size=nd)
+        out = list(doc)
+        while len(out) < L:
+            s = int(rng.integers(0, nd))
+            span = list(doc[s:s + int(rng.integers(4, 33))])
+            for i in range(len(span)):
+                if rng.random() < 0.1:
+                    span[i] = int(rng.integers(0, vocab))
+            out += span
+        hist[b, :L] = np.array(out[:L], dtype=np.int64)
+    return hist, lens

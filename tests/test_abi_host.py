@@ -170,3 +170,22 @@ def test_plug_validation_codes():
     assert plug(cap=0) == -2
     assert plug(B=-1) == -2
     assert plug(nxt=C(0x1002)) == -9      # int32 outputs must be 4-byte aligned
+
+
+def lookup(**kw):
+    a = dict(hist=FAKE, lens=FAKE, B=2, cap=100, mn=1, mx=3, k=5, drafts=FAKE, count=FAKE, stream=None)
+    a.update(kw)
+    return sv.library().spec_lookup_drafts(*a.values())
+
+
+def test_lookup_validation_codes():
+    assert lookup(B=0) == 0
+    assert lookup(hist=None) == -1
+    assert lookup(count=None) == -1
+    assert lookup(mn=0) == -2
+    assert lookup(mn=3, mx=2) == -2
+    assert lookup(mx=17) == -2
+    assert lookup(k=0) == -2
+    assert lookup(k=65) == -2
+    assert lookup(cap=0) == -2
+    assert lookup(drafts=C(0x1001)) == -9
