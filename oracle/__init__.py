@@ -21,7 +21,9 @@ the closed form for the mean emitted length under i.i.d. acceptance, the greedy
 identity, the worst and best cases the pages state, and scipy's softmax.  The token plug
 is pinned by its invariants (length arithmetic, untouched prefixes, capacity) and by a
 multi-step run whose history must equal the concatenated outputs; prompt lookup by
-hand-worked histories and by a search with Python's own substring find.
+hand-worked histories and by a search with Python's own substring find.  Lossless tree
+verification is pinned by a chi-square test of the whole emitted sequence against the
+target's own sequence law, which any tree rule that keeps that law must reproduce.
 """
 from .philox import philox4x64_10, uniforms  # noqa: F401
 from .verify import (  # noqa: F401
@@ -37,3 +39,4 @@ from .verify import (  # noqa: F401
 )
 from .plug import plug_tokens  # noqa: F401
 from .lookup import lookup_drafts  # noqa: F401
+from .tree_lossless import verify_tree_lossless  # noqa: F401
