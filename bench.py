@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="linear-b64-k5-v32000",
                     choices=["linear-b64-k5-v32000", "linear-b1-k4-v1024", "linear-b1000-k4-v1024",
-                             "linear-b256-k8-v128256", "greedy-b256-k8-v128256", "tree-b16-n61-v128256",
+                             "linear-b256-k8-v128256", "greedy-b256-k8-v128256", "tree-b16-n61-v128256", "tree-lossless-b16-n61-v128256",
                              "lmhead-b32-k5-h8192-v128256", "linear-b256-k1-v128256", "linear-plug-b64-k5-v32000",
                              "lookup-b64-l8192-n3-k5", "copy-probe"])
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -206,6 +206,8 @@ class Greedy(Linear):
 
 
 class Tree:
+    lossless = False
+
     def __init__(self, name, seeds):
         self.name = name
         self.seeds = seeds
@@ -222,9 +224,10 @@ class Tree:
         for c in range(1, self.N):
             depth[c] = depth[self.par[c]] + 1
         self.D = max(depth)
-        per_set = c0.logits.numel() * 2 + c0.draft_probs.numel() * 2
+        per_set = c0.logits.numel() * 2 + (0 if self.lossless else c0.draft_probs.numel() * 2)
         nsets = max(len(self.cases), int(np.ceil(rotate_bytes / per_set)))
-        self.sets = [(self.cases[i % len(self.cases)].logits.cuda(), self.cases[i % len(self.cases)].draft_probs.cuda(),
+        self.sets = [(self.cases[i % len(self.cases)].logits.cuda(),
+                      None if self.lossless else self.cases[i % len(self.cases)].draft_probs.cuda(),
                       self.cases[i % len(self.cases)].node_tokens.cuda()) for i in range(nsets)]
         self.tokens = torch.empty((self.B, self.D + 1), dtype=torch.int32, device="cuda")
         self.alen = torch.empty((self.B,), dtype=torch.int32, device="cuda")
@@ -234,13 +237,18 @@ class Tree:
 
     def launch(self, i):
         lg, q, t = self.sets[i % len(self.sets)]
-        self.sv.spec_verify_tree(lg, q, t, self.par, 1.0, 0, 0, self.tokens, self.alen, self.path, self.ws)
+        if self.lossless:
+            self.sv.spec_verify_tree_lossless(lg, t, self.par, 1.0, 0, 0, self.tokens, self.alen, self.path, self.ws)
+        else:
+            self.sv.spec_verify_tree(lg, q, t, self.par, 1.0, 0, 0, self.tokens, self.alen, self.path, self.ws)
 
     def positions(self):
         return self.B * (self.N - 1)
 
     def algorithmic_bytes(self):
-        return (self.B * self.N * self.V * 2 + self.B * (self.N - 1) * (2 + 4)
+        # every logits row once; the children's q(x) gathers (not read by the lossless
+        # rule), node tokens and outputs
+        return (self.B * self.N * self.V * 2 + self.B * (self.N - 1) * ((0 if self.lossless else 2) + 4)
                 + self.B * (self.D + 1) * 8 + self.B * 4)
 
     def config(self):
@@ -248,20 +256,28 @@ class Tree:
                 "logits_dtype": "bf16", "temperature": 1.0}
 
     def oracle_sample(self, budget_s):
-        from oracle import verify_tree
+        from oracle import verify_tree, verify_tree_lossless
         from synthetic import to_numpy_f64
         c = self.cases[0]
         L = to_numpy_f64(c.logits)
-        Q = to_numpy_f64(c.draft_probs)
+        Q = None if self.lossless else to_numpy_f64(c.draft_probs)
         T_ = c.node_tokens.numpy()
         done = 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             b = done % self.B
-            verify_tree(L[b:b + 1], Q[b:b + 1], T_[b:b + 1], c.parents, 1.0, 0, 0)
+            if self.lossless:
+                verify_tree_lossless(L[b:b + 1], T_[b:b + 1], c.parents, 1.0, 0, 0)
+            else:
+                verify_tree(L[b:b + 1], Q[b:b + 1], T_[b:b + 1], c.parents, 1.0, 0, 0)
             done += 1
         el = time.perf_counter() - t0
         return done * (self.N - 1) / el, f"{done} sequences, one at a time"
+
+
+class TreeLossless(Tree):
+    """The same 61-node tree and inputs, verified by the lossless sibling rule (no q rows)."""
+    lossless = True
 
 
 class LMHead:
@@ -420,6 +436,8 @@ def make_workload(name):
         return Greedy(name, lambda s: cfg3_case(seed=s), [3], "bf16", 0.7)
     if name == "tree-b16-n61-v128256":
         return Tree(name, [5, 105])
+    if name == "tree-lossless-b16-n61-v128256":
+        return TreeLossless(name, [5, 105])
     if name == "lmhead-b32-k5-h8192-v128256":
         return LMHead()
     if name == "lookup-b64-l8192-n3-k5":
@@ -520,7 +538,8 @@ def main():
     else:
         kernel_ms = extra.get("verify_ms", ms_step)  # with the plug: the verification kernel alone
         achieved = wl.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
-        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel"}.get(type(wl).__name__,
+        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel",
+                 "TreeLossless": "row_verify_kernel(tree, lossless)"}.get(type(wl).__name__,
                                                                                    "row_verify_kernel(linear)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),

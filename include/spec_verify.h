@@ -137,6 +137,32 @@ SV_API int spec_verify_tree(const void* target_logits, int lt, const void* draft
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Lossless static-tree verification: the same tree as spec_verify_tree, with candidates
+ * that are fixed top-K draft tokens ("Accelerating Sonar through speculation", section
+ * "EAGLE": Top-K candidates at every node), verified so that the emitted tokens follow
+ * the target law exactly ("Speculative decoding explained", section "Draft and
+ * verification loop"; the pages give no multi-candidate procedure, this is a reading).
+ * No draft probabilities are read: each candidate's draft law is a point mass.
+ *
+ * From the root, at node u with children c_1..c_m (sibling order) and p = p_u: child c_i
+ * (token x) is kept iff x is in [0, V), no earlier sibling has token x, and
+ * u_acc(b, c_i) * W_i < p(x), where W_i = 1 - sum of p over the distinct valid tokens of
+ * c_1..c_{i-1} (summed in sibling order).  The first kept child is the next node; if none
+ * is kept the extra token is drawn by inverse CDF with u_smp(b, u) from p with the
+ * children's valid tokens removed (from p itself when u has no children, or when the
+ * remaining mass is 0 through rounding).
+ *
+ *   target_logits [B, N, V] (lt), node_tokens [B, N], parent_host [N] (HOST): as for
+ *   spec_verify_tree.  Outputs and workspace (SV_KIND_TREE): as for spec_verify_tree;
+ *   out_accept_len is the depth of the node where the walk stopped.
+ */
+SV_API int spec_verify_tree_lossless(const void* target_logits, int lt, const int32_t* node_tokens,
+                       const int32_t* parent_host, int32_t B, int32_t N, int32_t V,
+                       float temperature, uint64_t seed, uint64_t offset,
+                       int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_path,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * LM-head projection feeding linear verification ("Accelerating Sonar through
  * speculation", sections "EAGLE" and "Training MTP heads": the heads share the target's
  * LM head, ~2 GB in bf16 for a 70B model).

@@ -1,5 +1,5 @@
 """MI355X (gfx950) speculative verification library: linear speculative sampling, greedy
-and static-tree verification, and an LM-head projection feeding verification, behind a
+and static-tree verification (plus a lossless tree variant), and an LM-head projection feeding verification, behind a
 small C ABI (include/spec_verify.h), plus an on-device token plug for the next step and
 prompt-lookup drafting.  This package is the thin Python binding over it."""
 from ._lib import (  # noqa: F401
@@ -21,5 +21,6 @@ from ._lib import (  # noqa: F401
     spec_verify_linear,
     spec_verify_strerror,
     spec_verify_tree,
+    spec_verify_tree_lossless,
     spec_verify_workspace_bytes,
 )

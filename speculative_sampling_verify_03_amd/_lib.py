@@ -23,7 +23,8 @@ ERRORS = {
     0: "SV_OK", -1: "SV_E_NULL", -2: "SV_E_SHAPE", -3: "SV_E_DTYPE", -4: "SV_E_TEMP",
     -5: "SV_E_TREE", -6: "SV_E_WORKSPACE", -7: "SV_E_DEVICE", -8: "SV_E_LAUNCH", -9: "SV_E_ALIGN",
 }
-EXPORTS = ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
+EXPORTS = ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
+           "spec_lmhead_verify",
            "spec_plug_tokens", "spec_lookup_drafts", "spec_verify_workspace_bytes", "spec_verify_strerror")
 
 
@@ -53,11 +54,14 @@ def _lib():
         lib.spec_verify_greedy.argtypes = [_P, ctypes.c_int, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
         lib.spec_verify_tree.argtypes = [_P, ctypes.c_int, _P, ctypes.c_int, _P, _P, _I32, _I32, _I32, _F32,
                                          _U64, _U64, _P, _P, _P, _P, _SZ, _P]
+        lib.spec_verify_tree_lossless.argtypes = [_P, ctypes.c_int, _P, _P, _I32, _I32, _I32, _F32,
+                                                  _U64, _U64, _P, _P, _P, _P, _SZ, _P]
         lib.spec_lmhead_verify.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _F32,
                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]
         lib.spec_plug_tokens.argtypes = [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
         lib.spec_lookup_drafts.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
-        for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_lmhead_verify",
+        for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
+                   "spec_lmhead_verify",
                    "spec_plug_tokens", "spec_lookup_drafts"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.spec_verify_workspace_bytes.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32]
@@ -200,6 +204,23 @@ def spec_verify_tree(target_logits, draft_probs, node_tokens, parents, temperatu
         _i32(out_accept_len, (B,), "out_accept_len"), _i32(out_path, (B, D + 1), "out_path"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_verify_tree")
+
+
+def spec_verify_tree_lossless(target_logits, node_tokens, parents, temperature, seed, offset,
+                              out_tokens, out_accept_len, out_path=None, workspace=None, stream=None):
+    """target_logits [B, N, V]; node_tokens int32 [B, N]; parents: host sequence of N ints
+    (BFS order, parents[0] = -1); outputs [B, D+1], [B], [B, D+1].  No draft
+    probabilities: each node's token is a fixed top-K candidate."""
+    B, N, V = target_logits.shape
+    par = (ctypes.c_int32 * N)(*[int(x) for x in parents])
+    D = out_tokens.shape[1] - 1
+    rc = _lib().spec_verify_tree_lossless(
+        _ptr(target_logits), _dt(target_logits), _i32(node_tokens, (B, N), "node_tokens"),
+        ctypes.cast(par, ctypes.c_void_p), B, N, V, float(temperature), int(seed), int(offset),
+        _i32(out_tokens, (B, D + 1), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"),
+        _i32(out_path, (B, D + 1), "out_path"),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(rc, "spec_verify_tree_lossless")
 
 
 def spec_lmhead_verify(hidden, lm_head, draft_probs, draft_tokens, temperature, seed, offset, logits_out,

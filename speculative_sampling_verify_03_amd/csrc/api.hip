@@ -34,7 +34,7 @@ int head_max(const void* p, int32_t V, int dt) {
   return ve - 1;
 }
 
-int run_rows(bool tree, const void* logits, int lt, const void* probs, int qt, const int32_t* tokens,
+int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* probs, int qt, const int32_t* tokens,
              int32_t B, int32_t R, int32_t k, int32_t V, float T, uint64_t seed, uint64_t offset,
              int32_t* out_tokens, int32_t* out_len, float* tprob, float* aprob, int32_t* out_path,
              const sv::TreeInfo* ti, void* ws, hipStream_t st) {
@@ -75,7 +75,7 @@ int run_rows(bool tree, const void* logits, int lt, const void* probs, int qt, c
   }
   // How the residual reads q rows (see launch_rows): every logits row must have the same
   // 16-byte phase (whole-vector pitch), and the matching q chunks must line up with it.
-  int qmode = 0;
+  int qmode = lossless ? 3 : 0;  // 3: the lossless tree, which reads no q rows
   const uintptr_t la = reinterpret_cast<uintptr_t>(logits), qa = reinterpret_cast<uintptr_t>(probs);
   if (!tree && k > 0) {
     if (lt == qt && (static_cast<int64_t>(V) * (bf16 ? 2 : 4)) % 16 == 0 && (la & 15) == (qa & 15)) {
@@ -103,7 +103,7 @@ int spec_verify_linear(const void* target_logits, int lt, const void* draft_prob
                                out_tokens, out_accept_len, workspace, workspace_bytes);
   if (rc != SV_OK || B == 0) return rc;
   if ((rc = check_device())) return rc;
-  return run_rows(false, target_logits, lt, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature,
+  return run_rows(false, false, target_logits, lt, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature,
                   seed, offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr,
                   nullptr, workspace, static_cast<hipStream_t>(stream));
 }
@@ -144,7 +144,21 @@ int spec_verify_tree(const void* target_logits, int lt, const void* draft_probs,
                              out_tokens, out_accept_len, workspace, workspace_bytes, &ti);
   if (rc != SV_OK || B == 0) return rc;
   if ((rc = check_device())) return rc;
-  return run_rows(true, target_logits, lt, draft_probs, qt, node_tokens, B, N, 0, V, temperature, seed, offset,
+  return run_rows(true, false, target_logits, lt, draft_probs, qt, node_tokens, B, N, 0, V, temperature, seed, offset,
+                  out_tokens, out_accept_len, nullptr, nullptr, out_path, &ti, workspace,
+                  static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_tree_lossless(const void* target_logits, int lt, const int32_t* node_tokens,
+                              const int32_t* parent_host, int32_t B, int32_t N, int32_t V, float temperature,
+                              uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_accept_len,
+                              int32_t* out_path, void* workspace, size_t workspace_bytes, void* stream) {
+  sv::TreeInfo ti;
+  int rc = sv::validate_tree_lossless(target_logits, lt, node_tokens, parent_host, B, N, V, temperature, out_tokens,
+                                      out_accept_len, workspace, workspace_bytes, &ti);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  return run_rows(true, true, target_logits, lt, nullptr, lt, node_tokens, B, N, 0, V, temperature, seed, offset,
                   out_tokens, out_accept_len, nullptr, nullptr, out_path, &ti, workspace,
                   static_cast<hipStream_t>(stream));
 }
@@ -162,7 +176,7 @@ int spec_lmhead_verify(const void* hidden, const void* lm_head, const void* draf
   (void)hipGetLastError();
   if (sv::launch_lmhead_gemm(hidden, lm_head, logits_out, B * (k + 1), H, V, st) != hipSuccess)
     return SV_E_LAUNCH;
-  return run_rows(false, logits_out, SV_F32, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature, seed,
+  return run_rows(false, false, logits_out, SV_F32, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature, seed,
                   offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr, nullptr,
                   workspace, st);
 }

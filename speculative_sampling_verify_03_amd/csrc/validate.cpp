@@ -153,6 +153,21 @@ int validate_tree(const void* logits, int lt, const void* probs, int qt, const i
   return check_ws(ws, ws_bytes, SV_KIND_TREE, B, N, V, 0);
 }
 
+int validate_tree_lossless(const void* logits, int lt, const int32_t* node_tokens, const int32_t* parent_host,
+                           int32_t B, int32_t N, int32_t V, float T, const int32_t* out_tokens,
+                           const int32_t* out_len, const void* ws, size_t ws_bytes, TreeInfo* tree) {
+  int rc;
+  if ((rc = check_dtype(lt))) return rc;
+  if ((rc = check_rows(B, N, V))) return rc;
+  if ((rc = check_temperature(T))) return rc;
+  if ((rc = build_tree(parent_host, N, tree))) return rc;
+  if (B == 0) return SV_OK;
+  if (!logits || !out_tokens || !out_len) return SV_E_NULL;
+  if (N > 1 && !node_tokens) return SV_E_NULL;
+  if ((rc = check_aligned(logits, lt))) return rc;
+  return check_ws(ws, ws_bytes, SV_KIND_TREE, B, N, V, 0);
+}
+
 int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt, const int32_t* tokens,
                     int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
                     const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes) {

@@ -47,6 +47,9 @@ int validate_tree(const void* logits, int lt, const void* probs, int qt, const i
                   const int32_t* parent_host, int32_t B, int32_t N, int32_t V, float T,
                   const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes,
                   TreeInfo* tree);
+int validate_tree_lossless(const void* logits, int lt, const int32_t* node_tokens, const int32_t* parent_host,
+                           int32_t B, int32_t N, int32_t V, float T, const int32_t* out_tokens,
+                           const int32_t* out_len, const void* ws, size_t ws_bytes, TreeInfo* tree);
 int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt, const int32_t* tokens,
                     int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
                     const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes);

@@ -20,6 +20,12 @@
 //      post an atomic max of the inverted key (row, token).  Tree: accepted children go
 //      into a node mask, candidates into per-node slots.
 // A single launch covers the whole step.
+//
+// The lossless tree variant (QMODE kQLossless) tests a node's children in sibling order,
+// each against the target mass left after the earlier siblings were rejected, keeps only
+// the first that passes, and draws the extra token from p without the children's tokens.
+// Each node's outcome depends on its own row only, so the rows still run independently;
+// the one kept child per node makes the alive set a single path.
 
 #include "sv_device.hpp"
 #include "sv_launch.hpp"
@@ -41,7 +47,9 @@ __device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
 //   kQHalf float32 logits with bfloat16 q whose 8-byte chunks line up with the logits
 //          vectors (the fused LM-head case): one 8-byte load per vector;
 //   kQElem anything else: element loads.
-constexpr int kQElem = 0, kQVec = 1, kQHalf = 2;
+// kQLossless is the lossless tree: no q rows at all (each candidate is a fixed top-K
+// token, so its draft law is a point mass).
+constexpr int kQElem = 0, kQVec = 1, kQHalf = 2, kQLossless = 3;
 
 // Occupancy target: at least two waves per SIMD (up to 256 VGPRs).  Holding the
 // 512-thread configurations to 128 VGPRs (two workgroups per CU) spilled the linear
@@ -71,6 +79,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   __shared__ int s_flag, s_y, s_last;
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
+  constexpr bool LOSSLESS = TREE && QMODE == kQLossless;
+  __shared__ int s_xtok[LOSSLESS ? 64 : 1];  // lossless: the children's valid tokens
+  __shared__ int s_nx;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -145,7 +156,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       g_valid = (g_x >= 0 && g_x < V);
       if (g_valid) {
         g_l = load_elem(rowp, g_x, BF16);
-        g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
+        if (!LOSSLESS) g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
       }
       draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
     }
@@ -182,9 +193,11 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 
   // ---- acceptance tests: keep x iff u_acc * q(x) < p(x), with p(x) in double
   bool acc = false;
+  double g_px = 0.0;
   if (g_node >= 0) {
     double px = 0.0;
     if (g_valid) px = exp((static_cast<double>(g_l) - static_cast<double>(m)) / P.T) / static_cast<double>(Z);
+    g_px = px;
     acc = g_valid && (static_cast<double>(g_uacc) * static_cast<double>(g_q) < px);
     if (!TREE) {
       const size_t o = static_cast<size_t>(b) * P.k + j;
@@ -199,7 +212,39 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   }
   uint64_t child_acc = 0;  // tree: this node's accepted children, as node bits (wave 0)
   uint64_t rej_dep = 0;    // linear: value returned by the rejection publish (waited on later)
-  if (TREE) {
+  if (LOSSLESS) {
+    if (wid == 0) {
+      // Sibling i (lane i) is tested against W_i = 1 - (mass of the distinct valid tokens
+      // of siblings 0..i-1, summed in sibling order): keep with probability p(x) / W_i.
+      // A repeated token has lost its mass with the earlier sibling and is never kept.
+      const int nch = s_nc[j];
+      bool dup = false;
+      for (int l = 0; l < nch; ++l) {
+        const int xl = __shfl(g_x, l);  // every lane takes part: the source lane must be active
+        dup = dup || (l < lane && xl == g_x);
+      }
+      const double contrib = (g_valid && !dup) ? g_px : 0.0;
+      const int64_t cbits = __double_as_longlong(contrib);
+      const int clo = static_cast<int>(cbits), chi = static_cast<int>(cbits >> 32);
+      double before = 0.0;
+      for (int l = 0; l < nch; ++l) {
+        const int64_t bl = (static_cast<int64_t>(__shfl(chi, l)) << 32) | static_cast<uint32_t>(__shfl(clo, l));
+        if (l < lane) before += __longlong_as_double(bl);
+      }
+      const double W = 1.0 - before;
+      acc = g_node >= 0 && g_valid && !dup && W > 0.0 && static_cast<double>(g_uacc) * W < g_px;
+      const uint64_t am = __ballot(acc);
+      child_acc = am ? 1ull << (s_fc[j] + __ffsll(static_cast<long long>(am)) - 1) : 0ull;
+      // the children's valid tokens leave this node's draw
+      const bool vx = g_node >= 0 && g_valid;
+      const uint64_t vm = __ballot(vx);
+      if (vx) s_xtok[__popcll(vm & ((1ull << lane) - 1ull))] = g_x;
+      if (lane == 0) {
+        s_nx = __popcll(vm);
+        s_flag = (child_acc == 0ull);
+      }
+    }
+  } else if (TREE) {
     if (wid == 0) {
       child_acc = __ballot(acc) << s_fc[j];
       if (lane == 0) s_flag = (child_acc == 0ull);
@@ -240,7 +285,11 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   if (s_flag) {
     const float u_smp = s_usmp;
     const float invZ = 1.0f / Z;
+    // linear: the residual at a rejected position
     bool resid = !TREE && (j < P.k);
+    // lossless tree: p without the children's tokens
+    bool masked = LOSSLESS && s_nx > 0;
+    const int nx = LOSSLESS ? s_nx : 0;
     const char* qrowp = static_cast<const char*>(P.probs) +
                         (static_cast<size_t>(b) * (TREE ? P.R : P.k) + j) * V * qeb;
     const uintptr_t qa = reinterpret_cast<uintptr_t>(qrowp);
@@ -258,9 +307,30 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       }
       return v;
     };
+    // Lossless tree: bit i of the result is set when this thread's vector v0 + i * kWave
+    // holds one of the children's tokens (rare: only those vectors take the masking loop).
+    auto excl_slots = [&](int v0) -> uint32_t {
+      uint32_t hit = 0;
+      for (int ci = 0; ci < nx; ++ci) {
+        const int d = (s_xtok[ci] + h) / VE - v0;
+        if (d >= 0 && d < NV * kWave && (d & (kWave - 1)) == 0) hit |= 1u << (d / kWave);
+      }
+      return hit;
+    };
+    // Lossless tree: does unit q (tile q / NW, wave q % NW) hold one of the children's tokens?
+    auto unit_has_child = [&](int q) -> bool {
+      bool any = false;
+      for (int ci = 0; ci < nx; ++ci) {
+        const int vc = (s_xtok[ci] + h) / VE;
+        any = any || (vc / TILE) * NW + (vc % TILE) / (NV * kWave) == q;
+      }
+      return any;
+    };
     // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
-    // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0)
-    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w) {
+    // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0), or
+    // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`excl`: this
+    // vector holds one of them)
+    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w, bool excl = false) {
       const int e0 = vi * VE - h;
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
@@ -273,6 +343,14 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           x = fmaxf(0.f, x * invZ - q);
         }
         w[e] = x;
+      }
+      if (masked && excl) {
+        for (int ci = 0; ci < nx; ++ci) {
+          const int d = s_xtok[ci] - e0;
+#pragma unroll
+          for (int e = 0; e < VE; ++e)
+            if (d == e) w[e] = 0.f;
+        }
       }
     };
     // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total.  With
@@ -291,6 +369,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) buf[i] = ld16_any(vrow, v0 + i * kWave, nvec);
       }
+      const uint32_t xs = masked ? excl_slots(v0) : 0u;
 #pragma unroll
       for (int g0 = 0; g0 < NV; g0 += G) {
         Vec16 qv[G] = {};
@@ -305,7 +384,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float w[VE];
-          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w);
+          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w, ((xs >> (g0 + g)) & 1u) != 0u);
           float sgm = 0.f;
 #pragma unroll
           for (int e = 0; e < VE; ++e) sgm += w[e];
@@ -339,21 +418,31 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       bool clamp = false;
       int tile_s = 0, wave_s = 0;
       const int first = loaded_tile;
-      for (int step = resid ? 0 : P.ntiles; step <= P.ntiles; ++step) {
+      // A masked draw (lossless tree) takes the pass-1 partials for every unit except the
+      // few that hold a child's token; their owning waves recompute them with the mask.
+      // s_tot < 0 marks a unit that was not recomputed.
+      if (masked) {
+        for (int q = tid; q < nunits; q += NT) s_tot[q] = -1.f;
+        __syncthreads();
+      }
+      for (int step = (resid || masked) ? 0 : P.ntiles; step <= P.ntiles; ++step) {
         int tile;
         bool active;
         if (step < P.ntiles) {
           tile = (first + step) % P.ntiles;
-          active = true;
+          active = resid || (masked && unit_has_child(tile * NW + wid));
         } else {
-          if (resid) __syncthreads();
+          if (resid || masked) __syncthreads();
           // weight of each (tile, wave) unit: the residual totals, or for a draw from p
           // itself the pass-1 partials rescaled to the row max (nothing recomputed)
-          auto unit = [&](int q) -> float { return resid ? s_tot[q] : s_ps[q] * fast_exp2((s_pm[q] - m) * c); };
+          auto unit = [&](int q) -> float {
+            if (resid || (masked && s_tot[q] >= 0.f)) return s_tot[q];
+            return s_ps[q] * fast_exp2((s_pm[q] - m) * c);
+          };
           // every thread walks the units in the same order: S, then the winning unit
           float S = 0.f;
           for (int q = 0; q < nunits; ++q) S += unit(q);
-          if (S <= 0.f) {  // residual empty through rounding: draw from p itself
+          if (S <= 0.f) {  // residual or remainder empty through rounding: draw from p itself
             empty = true;
             break;
           }
@@ -392,8 +481,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
       }
       if (empty) {
-        if (!resid) break;
+        if (!resid && !masked) break;
         resid = false;
+        masked = false;
         continue;
       }
       if (wid == wave_s) {
@@ -436,7 +526,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         if (lane == lstar) {
           const int vi = v0 + istar * kWave;
           float w[VE];
-          weights(mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V), load_q(vi), vi, w);
+          const bool ex = masked && ((excl_slots(v0) >> istar) & 1u);
+          weights(mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V), load_q(vi), vi, w, ex);
           const double t3 = t2 - (lstar > 0 ? static_cast<double>(excl) : 0.0);
           int y = -1, ylast = -1;
           float ec = 0.f;
@@ -601,7 +692,10 @@ RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows) {
 
 hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,
                        int grid, hipStream_t st) {
-  if (tree)  // the tree draws its extra token from p alone and never reads q rows
+  if (tree && qmode == kQLossless)
+    return bf16 ? launch_rows_t<true, true, kQLossless>(P, td, cfg, grid, st)
+                : launch_rows_t<false, true, kQLossless>(P, td, cfg, grid, st);
+  if (tree)  // the tree draws its extra token from p alone; q is read at the children only
     return bf16 ? launch_rows_t<true, true, kQElem>(P, td, cfg, grid, st)
                 : launch_rows_t<false, true, kQElem>(P, td, cfg, grid, st);
   if (bf16)

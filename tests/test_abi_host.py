@@ -136,6 +136,29 @@ def test_tree_validation_codes():
     assert tree([-1, 0], wsb=4) == -6
 
 
+def tree_lossless(parents, **kw):
+    par = (ctypes.c_int32 * len(parents))(*parents) if parents is not None else None
+    a = dict(logits=FAKE, lt=1, toks=FAKE, par=ctypes.cast(par, C) if par else None,
+             B=2, N=len(parents) if parents else 3, V=100, T=1.0, seed=0, off=0, out=FAKE, alen=FAKE,
+             path=None, ws=FAKE_WS, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return sv.library().spec_verify_tree_lossless(*a.values())
+
+
+def test_tree_lossless_validation_codes():
+    assert tree_lossless([-1, 0, 0, 1], B=0) == 0
+    assert tree_lossless(None, N=3) == -1
+    assert tree_lossless([-1, 0, 0], toks=None) == -1
+    assert tree_lossless([-1], toks=None, wsb=1 << 20) != -1   # a root-only tree reads no tokens
+    assert tree_lossless([-1, 1, 0]) == -5
+    assert tree_lossless([-1, 0, 1, 0]) == -5
+    assert tree_lossless([-1] + [0] * 64) == -2
+    assert tree_lossless([-1, 0], lt=7) == -3
+    assert tree_lossless([-1, 0], T=float("nan")) == -4
+    assert tree_lossless([-1, 0], wsb=4) == -6
+    assert tree_lossless([-1, 0], logits=C(0x1001)) == -9
+
+
 def lmhead(**kw):
     a = dict(h=C(0x1000), w=FAKE, probs=FAKE, qt=1, toks=FAKE, B=2, k=3, H=128, V=100, T=1.0, seed=0,
              off=0, logits=FAKE, out=FAKE, alen=FAKE, tp=None, ap=None, ws=FAKE_WS, wsb=1 << 20, stream=None)
