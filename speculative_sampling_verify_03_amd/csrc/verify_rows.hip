@@ -52,16 +52,21 @@ __device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
 constexpr int kQElem = 0, kQVec = 1, kQHalf = 2, kQLossless = 3;
 
 // Occupancy target: at least two waves per SIMD (up to 256 VGPRs).  Holding the
-// 512-thread configurations to 128 VGPRs (two workgroups per CU) spilled the linear
-// instantiations to scratch; with a whole tile's loads in flight per thread one
-// workgroup per CU already keeps enough bytes moving.
-template <int NT>
+// multi-tile 512 x 16 configurations to 128 VGPRs (two workgroups per CU) spilled the
+// linear instantiations to scratch; with a whole tile's loads in flight per thread one
+// workgroup per CU already keeps enough bytes moving there.
+template <int NT, int NV>
 struct RowOccupancy {
   static constexpr int kWavesPerEU = 2;
 };
+// 512 x 8 rows are single-tile: two workgroups per CU (128 VGPRs) fit without spilling.
+template <>
+struct RowOccupancy<512, 8> {
+  static constexpr int kWavesPerEU = 4;
+};
 
 template <bool BF16, int NT, int NV, bool TREE, int QMODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RowOccupancy<NT>::kWavesPerEU)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RowOccupancy<NT, NV>::kWavesPerEU)))
 void row_verify_kernel(RowParams P, TreeDesc td) {
   using E = Elem<BF16>;
   constexpr int VE = E::kPerVec;
@@ -506,6 +511,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           istar = ilast < 0 ? 0 : ilast;
           clamp = true;
         }
+        // The winning slot's logits are in buf (this wave's share of tile_s is what buf
+        // holds now); no reload.  A 16-byte q vector is loaded before the lane scan, so
+        // that its latency overlaps the scan.
+        const int vis = v0 + istar * kWave;
+        const Vec16 qs = QMODE == kQVec ? load_q(vis) : Vec16{};
+        Vec16 ls = buf[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i)
+          if (i == istar) ls = buf[i];
         // lane inside the slot: the slot's scan again (same inputs, same values)
         float sg = 0.f;
 #pragma unroll
@@ -524,10 +538,10 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
         const float excl = lane_value(scan, lstar > 0 ? lstar - 1 : 0);
         if (lane == lstar) {
-          const int vi = v0 + istar * kWave;
+          const int vi = vis;
           float w[VE];
           const bool ex = masked && ((excl_slots(v0) >> istar) & 1u);
-          weights(mask_edges<BF16>(ld16(vrow, vi, nvec), vi * VE - h, V), load_q(vi), vi, w, ex);
+          weights(ls, QMODE == kQVec ? qs : load_q(vi), vi, w, ex);
           const double t3 = t2 - (lstar > 0 ? static_cast<double>(excl) : 0.0);
           int y = -1, ylast = -1;
           float ec = 0.f;
