@@ -60,13 +60,16 @@ struct RowOccupancy {
   static constexpr int kWavesPerEU = 2;
 };
 // 512 x 8 rows are single-tile: two workgroups per CU (128 VGPRs) fit without spilling.
+// The lossless tree is held to 128 VGPRs too (a few bytes of spill): four 256-thread
+// workgroups per CU keep a 976-row step (16 trees of 61 nodes) resident in one round,
+// which measured 78 us against 87 us at 137 VGPRs.
 template <>
 struct RowOccupancy<512, 8> {
   static constexpr int kWavesPerEU = 4;
 };
 
 template <bool BF16, int NT, int NV, bool TREE, int QMODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RowOccupancy<NT, NV>::kWavesPerEU)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(QMODE == kQLossless ? 4 : RowOccupancy<NT, NV>::kWavesPerEU)))
 void row_verify_kernel(RowParams P, TreeDesc td) {
   using E = Elem<BF16>;
   constexpr int VE = E::kPerVec;
@@ -312,15 +315,27 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       }
       return v;
     };
-    // Lossless tree: bit i of the result is set when this thread's vector v0 + i * kWave
-    // holds one of the children's tokens (rare: only those vectors take the masking loop).
-    auto excl_slots = [&](int v0) -> uint32_t {
-      uint32_t hit = 0;
+    // Lossless tree: bit i * VE + e of em[] is set when element e of this thread's vector
+    // v0 + i * kWave is one of the children's tokens (rare: a vector with no bit set is
+    // never touched by the mask).
+    constexpr int kMaskWords = (NV * VE + 31) / 32;
+    auto excl_bits = [&](int v0, uint32_t (&em)[kMaskWords]) {
+#pragma unroll
+      for (int k = 0; k < kMaskWords; ++k) em[k] = 0u;
       for (int ci = 0; ci < nx; ++ci) {
-        const int d = (s_xtok[ci] + h) / VE - v0;
-        if (d >= 0 && d < NV * kWave && (d & (kWave - 1)) == 0) hit |= 1u << (d / kWave);
+        const int pos = s_xtok[ci] + h;  // element position in the vector-aligned stream
+        const int d = pos / VE - v0;
+        if (d >= 0 && d < NV * kWave && (d & (kWave - 1)) == 0) {
+          const int bit = (d / kWave) * VE + (pos - (pos / VE) * VE);
+#pragma unroll
+          for (int k = 0; k < kMaskWords; ++k)
+            if (k == bit / 32) em[k] |= 1u << (bit & 31);
+        }
       }
-      return hit;
+    };
+    // the VE mask bits of slot i (i known at compile time in the tile loops)
+    auto slot_bits = [&](const uint32_t (&em)[kMaskWords], int i) -> uint32_t {
+      return (em[(i * VE) / 32] >> ((i * VE) & 31)) & ((1u << VE) - 1u);
     };
     // Lossless tree: does unit q (tile q / NW, wave q % NW) hold one of the children's tokens?
     auto unit_has_child = [&](int q) -> bool {
@@ -333,9 +348,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     };
     // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
     // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0), or
-    // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`excl`: this
-    // vector holds one of them)
-    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w, bool excl = false) {
+    // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`xb`: the mask
+    // bits of this vector)
+    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w, uint32_t xb = 0u) {
       const int e0 = vi * VE - h;
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
@@ -349,13 +364,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
         w[e] = x;
       }
-      if (masked && excl) {
-        for (int ci = 0; ci < nx; ++ci) {
-          const int d = s_xtok[ci] - e0;
+      if (LOSSLESS) {  // branch free: a branch here kept every vector's weights live at once
 #pragma unroll
-          for (int e = 0; e < VE; ++e)
-            if (d == e) w[e] = 0.f;
-        }
+        for (int e = 0; e < VE; ++e) w[e] = ((xb >> e) & 1u) ? 0.f : w[e];
       }
     };
     // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total.  With
@@ -374,7 +385,12 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) buf[i] = ld16_any(vrow, v0 + i * kWave, nvec);
       }
-      const uint32_t xs = masked ? excl_slots(v0) : 0u;
+      uint32_t em[kMaskWords];
+      if (masked) excl_bits(v0, em);
+      else {
+#pragma unroll
+        for (int k = 0; k < kMaskWords; ++k) em[k] = 0u;
+      }
 #pragma unroll
       for (int g0 = 0; g0 < NV; g0 += G) {
         Vec16 qv[G] = {};
@@ -389,7 +405,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float w[VE];
-          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w, ((xs >> (g0 + g)) & 1u) != 0u);
+          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w, LOSSLESS ? slot_bits(em, g0 + g) : 0u);
           float sgm = 0.f;
 #pragma unroll
           for (int e = 0; e < VE; ++e) sgm += w[e];
@@ -540,8 +556,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         if (lane == lstar) {
           const int vi = vis;
           float w[VE];
-          const bool ex = masked && ((excl_slots(v0) >> istar) & 1u);
-          weights(ls, QMODE == kQVec ? qs : load_q(vi), vi, w, ex);
+          uint32_t xb = 0u;
+          if (masked) {
+            uint32_t em[kMaskWords];
+            excl_bits(v0, em);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+              if (i == istar) xb = slot_bits(em, i);
+          }
+          weights(ls, QMODE == kQVec ? qs : load_q(vi), vi, w, xb);
           const double t3 = t2 - (lstar > 0 ? static_cast<double>(excl) : 0.0);
           int y = -1, ylast = -1;
           float ec = 0.f;
