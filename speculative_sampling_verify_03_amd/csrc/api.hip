@@ -125,6 +125,19 @@ int spec_verify_greedy(const void* target_logits, int lt, const int32_t* draft_t
   P.V = V;
   P.k = k;
   P.S = sv::greedy_splits(B, k + 1, V);
+  // flat path: the tensor starts on a 16-byte boundary and every row is whole vectors
+  const int64_t row_bytes = static_cast<int64_t>(V) * (lt == SV_BF16 ? 2 : 4);
+  const int64_t nvec = row_bytes / 16;
+  P.flat = 0;
+  if (row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0 &&
+      static_cast<int64_t>(k + 1) * nvec < (int64_t(1) << 31)) {
+    const int64_t total = static_cast<int64_t>(B) * (k + 1) * nvec;
+    int64_t G = (total + sv::kGreedyFlatMinVectors - 1) / sv::kGreedyFlatMinVectors;
+    if (G > sv::kGreedyFlatMaxGroups) G = sv::kGreedyFlatMaxGroups;
+    P.flat = 1;
+    P.nvec = static_cast<int32_t>(nvec);
+    P.G = static_cast<int32_t>(G < 1 ? 1 : G);
+  }
   P.out_tokens = out_tokens;
   P.out_accept_len = out_accept_len;
   P.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.counters_off);

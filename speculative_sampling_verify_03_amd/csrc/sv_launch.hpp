@@ -58,6 +58,9 @@ struct GreedyParams {
   const void* logits;
   const int32_t* tokens;
   int32_t B, R, V, k, S;
+  // flat path (16-byte aligned base and rows): nvec vectors per row, G workgroups over
+  // the B * R * nvec vectors of the whole tensor; flat = 0 selects the per-row split path
+  int32_t flat, nvec, G;
   int32_t* out_tokens;
   int32_t* out_accept_len;
   uint32_t* counters;  // [B] arrival tickets (zero on entry and exit)
@@ -65,6 +68,9 @@ struct GreedyParams {
 };
 constexpr int kGreedyThreads = 256;
 constexpr int kGreedyUnroll = 8;
+constexpr int kGreedyFlatUnroll = 8;          // 16-byte loads in flight per thread
+constexpr int kGreedyFlatMaxGroups = 2048;   // eight 256-thread workgroups on each of 256 CUs
+constexpr int kGreedyFlatMinVectors = 2048;  // at least one full batch per thread and a half
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t st);
 
 // LM-head GEMM: logits[M, V] (fp32) = hidden[M, H] (bf16) @ W[H, V] (bf16).

@@ -6,14 +6,18 @@
 // Each row is split over S workgroups that stream their slice once with 16-byte loads
 // and reduce (value, lowest index); the slices of a row merge through an atomic max of an
 // orderable key, and the last workgroup of a sequence to arrive finds the first mismatch
-// with a ballot and writes the outputs.
+// with a ballot and writes the outputs.  Tensors whose rows are whole 16-byte vectors take
+// the flat path below instead (equal contiguous ranges of the whole tensor).
 
 #include <climits>
+#include <mutex>
 
 #include "sv_device.hpp"
 #include "sv_launch.hpp"
 
 namespace sv {
+
+__device__ void greedy_finish(const GreedyParams& P, int b, int lane);
 
 template <bool BF16>
 __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) {
@@ -85,7 +89,12 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) 
   __syncthreads();
   if (!s_last || wid != 0) return;
 
-  // last arrival: each row's argmax, then the first mismatch
+  greedy_finish(P, b, lane);  // last arrival
+}
+
+// Last arrival of sequence b: each row's argmax from its key word (which is cleared for
+// the next call), then the first mismatch by ballot, then the outputs.  One wave.
+__device__ void greedy_finish(const GreedyParams& P, int b, int lane) {
   const int k = P.k;
   int g = -1;
   if (lane < P.R) g = argmax_key_index(atomic_xchg_u64(&P.rowword[static_cast<size_t>(b) * P.R + lane], 0ull));
@@ -106,7 +115,129 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) 
   }
 }
 
-hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t st) {
+// Flat path, for a 16-byte aligned tensor whose rows are whole vectors: the B * R * nvec
+// vectors of the tensor are cut into G equal contiguous ranges, one per workgroup, so every
+// workgroup streams the same number of bytes and the grid fits the chip in one round.  A
+// range is walked in pieces that end at row boundaries; each piece's (value, lowest index)
+// goes into its row's key word with one atomic max, and its vector count into the
+// sequence's counter, so the piece that brings the count to R * nvec is the sequence's
+// last and writes its outputs.
+template <bool BF16>
+__global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParams P) {
+  using E = Elem<BF16>;
+  constexpr int VE = E::kPerVec;
+  constexpr int NT = kGreedyThreads;
+  constexpr int U = kGreedyFlatUnroll;
+  constexpr int NW = NT / kWave;
+  __shared__ float s_v[NW];
+  __shared__ int s_i[NW];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int64_t nvec = P.nvec;
+  const int64_t total = static_cast<int64_t>(P.B) * P.R * nvec;
+  const int64_t beg = total * blockIdx.x / P.G;
+  const int64_t end = total * (blockIdx.x + 1) / P.G;
+  const SV_GLOBAL Vec16* base = gptr<Vec16>(P.logits);
+  const uint32_t seq_vectors = static_cast<uint32_t>(P.R * nvec);
+
+  int64_t pos = beg;
+  int64_t r = beg / nvec;
+  while (pos < end) {
+    const int64_t row0 = r * nvec;
+    const int64_t piece_end = min(end, row0 + nvec);
+    const int n = static_cast<int>(piece_end - pos);    // vectors in this piece
+    const int first = static_cast<int>(pos - row0);     // its first vector inside the row
+    const SV_GLOBAL Vec16* pp = base + pos;
+    // Per thread: the largest vector maximum, the first of this thread's vectors (they
+    // ascend) that reaches it, and that vector's data; the element index is looked up once
+    // at the end.  A max per element instead of a (value, index) compare and select.
+    float best = -INFINITY;
+    int best_i = -1;
+    Vec16 best_v{};
+    for (int i0 = tid; i0 < n; i0 += NT * U) {
+      Vec16 t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = ld16(pp, i0 + u * NT, n);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        float vm = E::at(t[u], 0);
+#pragma unroll
+        for (int e = 1; e < VE; ++e) vm = fmaxf(vm, E::at(t[u], e));
+        const bool take = i < n && (vm > best || best_i < 0);
+        best = take ? vm : best;
+        best_i = take ? i : best_i;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) best_v.w[w] = take ? t[u].w[w] : best_v.w[w];
+      }
+    }
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    if (best_i >= 0) {
+      bv = best;
+#pragma unroll
+      for (int e = VE - 1; e >= 0; --e)
+        if (E::at(best_v, e) == best) bi = (first + best_i) * VE + e;
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      s_v[wid] = bv;
+      s_i[wid] = bi;
+    }
+    __syncthreads();
+    const int b = static_cast<int>(r / P.R);
+    if (tid == 0) {
+      float v = s_v[0];
+      int i = s_i[0];
+      for (int w = 1; w < NW; ++w) argmax_merge(v, i, s_v[w], s_i[w]);
+      const uint64_t old = atomic_max_u64(&P.rowword[r], argmax_key(v, i));
+      after_value(old);  // the key is in place before the count says so
+      const uint32_t prev = atomicAdd(&P.counters[b], static_cast<uint32_t>(n));
+      s_last = prev + static_cast<uint32_t>(n) == seq_vectors;
+    }
+    __syncthreads();  // also: s_v is rewritten by the next piece only after this
+    if (s_last && wid == 0) greedy_finish(P, b, lane);
+    pos = piece_end;
+    ++r;
+  }
+}
+
+// Workgroups of the flat kernel that the current device holds at once (occupancy x CUs),
+// cached per device and dtype; 0 if the runtime cannot say.
+static int flat_resident_groups(bool bf16) {
+  static std::mutex mu;
+  static int cache[64][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  int& c = cache[dev][bf16 ? 1 : 0];
+  if (c == 0) {
+    int per_cu = 0, cus = 0;
+    const hipError_t e1 = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, greedy_flat_kernel<true>,
+                                                                             kGreedyThreads, 0)
+                               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, greedy_flat_kernel<false>,
+                                                                             kGreedyThreads, 0);
+    const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e1 != hipSuccess || e2 != hipSuccess || per_cu < 1 || cus < 1) return 0;
+    c = per_cu * cus;
+  }
+  return c;
+}
+
+hipError_t launch_greedy(const GreedyParams& P0, bool bf16, hipStream_t st) {
+  if (P0.flat) {
+    // one round: no more workgroups than the chip holds at once
+    GreedyParams P = P0;
+    const int resident = flat_resident_groups(bf16);
+    if (resident > 0 && P.G > resident) P.G = resident;
+    if (bf16) hipLaunchKernelGGL(greedy_flat_kernel<true>, dim3(P.G), dim3(kGreedyThreads), 0, st, P);
+    else hipLaunchKernelGGL(greedy_flat_kernel<false>, dim3(P.G), dim3(kGreedyThreads), 0, st, P);
+    return hipGetLastError();
+  }
+  const GreedyParams& P = P0;
   const int grid = P.B * P.R * P.S;
   if (bf16) hipLaunchKernelGGL(greedy_kernel<true>, dim3(grid), dim3(kGreedyThreads), 0, st, P);
   else hipLaunchKernelGGL(greedy_kernel<false>, dim3(grid), dim3(kGreedyThreads), 0, st, P);

@@ -87,3 +87,13 @@ def test_tree_ragged_misaligned(misalign):
     case = tree_case(20, eagle_tree_parents((3, 2, 2), 64), 1003, seed=4, dtype="bf16", noise_sigma=0.8)
     got = run_tree(case, seed=5, misalign=misalign)
     check_tree(got, case, seed=5, what=f"tree V=1003 misalign={misalign}")
+
+
+@pytest.mark.parametrize("B,k,V,dtype", [(3, 4, 31992, "bf16"), (1, 0, 8, "bf16"), (7, 3, 4100, "f32"),
+                                         (100, 2, 1024, "bf16")])
+def test_greedy_flat_pieces_cross_rows(B, k, V, dtype):
+    # rows of whole 16-byte vectors take the flat path: equal ranges of the whole tensor
+    # whose boundaries fall inside rows, and rows shorter than one range
+    case = linear_case(B, k, V, seed=B + V, dtype=dtype, noise_sigma=0.05)
+    got = run_greedy(case.logits, case.greedy_tokens)
+    check_greedy(got, case.logits, case.greedy_tokens, what=f"greedy flat B={B} k={k} V={V} {dtype}")
