@@ -94,9 +94,13 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int r = blockIdx.x;
-  const int b = r / P.R;
-  const int j = r - b * P.R;
+  // Position-major dispatch: workgroup x takes row j = x / B of sequence b = x % B, so
+  // every sequence's early rows (where its first rejection, and so its costly residual
+  // draw, usually falls) start before the later rows, and a later row more often sees an
+  // earlier rejection published before it decides whether to draw.
+  const int j = static_cast<int>(blockIdx.x) / P.B;
+  const int b = static_cast<int>(blockIdx.x) - j * P.B;
+  const int r = b * P.R + j;
   const int V = P.V;
   const float c = P.c;
 
