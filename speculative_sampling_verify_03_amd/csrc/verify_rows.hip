@@ -144,11 +144,13 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   // ---- pass 1: online max / sum of 2^((l - m) c) over the row
   bool g_valid = false;
   float g_l = 0.f, g_q = 0.f, g_uacc = 0.f, g_usmp = 0.f;
-  // Linear multi-tile configurations (NV = 16) load tile t+1 while tile t is reduced, so a
-  // row's tiles stream back to back; single-tile configurations have nothing to prefetch,
-  // and the tree kernels gain more from the occupancy the second buffer would cost them
-  // (measured: 66 us with it off, 72 us on, for 61-node trees over V = 128256).
-  constexpr bool PIPE = (NV == 16) && !TREE;
+  // Linear multi-tile rows of 512 x 16 (few rows in the batch) load tile t+1 while tile t
+  // is reduced, so a row's tiles stream back to back.  Single-tile configurations have
+  // nothing to prefetch; the tree kernels gain more from the occupancy the second buffer
+  // would cost them (66 us with it off, 72 us on, for 61-node trees over V = 128256); and
+  // 256 x 16 rows (many rows, two workgroups per CU either way) measured faster without it
+  // (B=256 k=8 V=128256: 143 us against 148 us).
+  constexpr bool PIPE = (NV == 16) && !TREE && NT >= 512;
   Vec16 buf[NV];
   Vec16 nxt[PIPE ? NV : 1];
   auto load_tile = [&](Vec16* dst, int tile) {
