@@ -34,7 +34,8 @@ def _check(hist, lens, mn, mx, k, what):
 
 
 @pytest.mark.parametrize("B,cap,vocab,mn,mx,k", [(64, 4096, 32000, 1, 3, 5), (16, 2000, 50, 2, 4, 8),
-                                                 (200, 300, 7, 1, 16, 64), (8, 70000, 32000, 1, 2, 1)])
+                                                 (200, 300, 7, 1, 16, 64), (8, 70000, 32000, 1, 2, 1),
+                                                 (32, 3000, 20, 2, 6, 10)])
 def test_lookup_random(B, cap, vocab, mn, mx, k):
     announce(f"lookup B={B} cap={cap} vocab={vocab} n={mn}..{mx} k={k}")
     hist, lens = lookup_histories(B, cap, vocab=vocab, seed=B + cap)
@@ -63,3 +64,12 @@ def test_lookup_empty_batch():
     L = torch.empty((0,), dtype=torch.int32, device=DEV)
     sv.spec_lookup_drafts(H, L, 1, 3, torch.empty((0, 4), dtype=torch.int32, device=DEV),
                           torch.empty((0,), dtype=torch.int32, device=DEV))
+
+
+@pytest.mark.parametrize("seed", [7, 107])
+def test_lookup_bench_workload(seed):
+    # the benchmark's own inputs: B=64 histories of up to 8192 tokens, phrases of 1-3, 5 drafts
+    announce(f"lookup bench workload seed={seed}")
+    hist, lens = lookup_histories(64, 8192, seed=seed)
+    _check(hist, lens, 1, 3, 5, f"bench seed={seed}")
+
