@@ -7,7 +7,7 @@
 
 namespace sv {
 
-constexpr int kLookupThreads = 256;
+constexpr int kLookupThreads = 1024;
 constexpr int kLookupPer = 8;                              // end positions per thread and tile
 constexpr int kLookupTile = kLookupThreads * kLookupPer;   // end positions per tile
 constexpr int kLookupHalo = kMaxNgram;                     // tokens left of a tile's first end
