@@ -49,6 +49,12 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) 
   const int vbeg = s * chunk;
   const int vend = min(nvec, vbeg + chunk);
 
+  // Whole vectors: a max per element, and the first vector reaching the running maximum
+  // kept with its data (its element index looked up once at the end).  The row's first and
+  // last vectors may be partial: those take the exact per-element (value, index) merge.
+  float best = -INFINITY;
+  int best_vi = -1;
+  Vec16 best_v{};
   float bv = -INFINITY;
   int bi = INT_MAX;
   for (int base = vbeg + tid; base < vend; base += NT * U) {
@@ -63,12 +69,35 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) 
       const int vi = base + u * NT;
       const int e0 = vi * VE - h;
       const bool full = vi < vend && e0 >= 0 && e0 + VE <= V;
+      float vm = E::at(t[u], 0);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const bool ok = full || (vi < vend && e0 + e >= 0 && e0 + e < V);
-        if (ok) argmax_merge(bv, bi, E::at(t[u], e), e0 + e);
-      }
+      for (int e = 1; e < VE; ++e) vm = fmaxf(vm, E::at(t[u], e));
+      const bool take = full && (vm > best || best_vi < 0);
+      best = take ? vm : best;
+      best_vi = take ? vi : best_vi;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) best_v.w[w] = take ? t[u].w[w] : best_v.w[w];
     }
+  }
+  // The partial edge vectors (the row's first when it starts inside a vector, its last
+  // when it ends inside one) are merged element by element by the thread whose stride
+  // passed them, after the loop: a branch inside the loop kept every loaded vector live.
+  for (int ev = 0; ev < 2; ++ev) {
+    const int vi = ev == 0 ? 0 : nvec - 1;
+    const int e0 = vi * VE - h;
+    const bool partial = e0 < 0 || e0 + VE > V;
+    if (partial && vi >= vbeg && vi < vend && (vi - vbeg) % NT == tid && (ev == 0 || vi != 0)) {
+      const Vec16 t = ld16(vrow, vi, nvec);
+      for (int e = 0; e < VE; ++e)
+        if (e0 + e >= 0 && e0 + e < V) argmax_merge(bv, bi, E::at(t, e), e0 + e);
+    }
+  }
+  if (best_vi >= 0) {
+    int idx = INT_MAX;
+#pragma unroll
+    for (int e = VE - 1; e >= 0; --e)
+      if (E::at(best_v, e) == best) idx = best_vi * VE - h + e;
+    argmax_merge(bv, bi, best, idx);
   }
   wave_argmax(bv, bi);
   if (lane == 0) {

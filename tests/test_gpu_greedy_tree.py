@@ -97,3 +97,21 @@ def test_greedy_flat_pieces_cross_rows(B, k, V, dtype):
     case = linear_case(B, k, V, seed=B + V, dtype=dtype, noise_sigma=0.05)
     got = run_greedy(case.logits, case.greedy_tokens)
     check_greedy(got, case.logits, case.greedy_tokens, what=f"greedy flat B={B} k={k} V={V} {dtype}")
+
+
+@pytest.mark.parametrize("misalign", [0, 1, 5])
+def test_greedy_edge_vector_ties(misalign):
+    # rows that are not whole 16-byte vectors take the split path, whose first and last
+    # vectors are partial and merged element by element: equal maxima there and in a whole
+    # vector must still resolve to the lowest index
+    V = 1001
+    L = torch.zeros((4, 4, V), dtype=torch.bfloat16)
+    L[0, :, [0, 999]] = 3.0      # first element vs a later whole-vector element
+    L[1, :, [1000]] = 3.0        # only the last element
+    L[2, :, [3, 1000]] = 3.0     # an early element vs the last
+    L[3, :, :] = -1.0
+    L[3, :, [1000, 7]] = -0.5
+    X = torch.tensor([[0, 0, 0], [1000, 1000, 0], [3, 3, 3], [7, 7, 1000]], dtype=torch.int32)
+    got = run_greedy(L, X, misalign)
+    assert list(got["accept_len"]) == [3, 2, 3, 2]
+    check_greedy(got, L, X, what=f"greedy edge ties misalign={misalign}")
