@@ -538,7 +538,7 @@ def main():
     else:
         kernel_ms = extra.get("verify_ms", ms_step)  # with the plug: the verification kernel alone
         achieved = wl.algorithmic_bytes() / (kernel_ms * 1e-3) / 1e9
-        kname = {"Greedy": "greedy_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel",
+        kname = {"Greedy": "greedy_flat_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel",
                  "TreeLossless": "row_verify_kernel(tree, lossless)"}.get(type(wl).__name__,
                                                                                    "row_verify_kernel(linear)")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
