@@ -100,6 +100,13 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i, bool bf1
   return gptr<float>(base)[i];
 }
 
+// A 32-bit load issued where it stands: as a relaxed atomic it is an ordered access that
+// the compiler does not sink to the value's first use (plain loads were moved past the
+// atomics their value does not depend on, which added a round trip).
+__device__ __forceinline__ int load_early_i32(const int32_t* p) {
+  return __hip_atomic_load((SV_GLOBAL int32_t*)(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // 2^x with the hardware transcendental (v_exp_f32, ~1 ulp).  Results below 2^-126 flush
 // to zero, which only drops terms smaller than 2^-126 of the row maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
