@@ -145,6 +145,34 @@ def test_deterministic_and_workspace_reuse():
     assert np.array_equal(c["tokens"], a["tokens"][:10])
 
 
+@pytest.mark.parametrize("what", ["single-tile", "multi-tile", "every row rejects"])
+def test_workspace_returns_to_zero(what):
+    # Rejected rows post their position to a per-sequence word before drawing, and the
+    # finishing workgroup clears it after every row's ticket: the whole workspace must be
+    # zero after a call, so that the next call starts clean (and so must its results).
+    import speculative_sampling_verify_03_amd as sv
+    if what == "single-tile":
+        case = linear_case(64, 5, 32000, seed=31, dtype="bf16", noise_sigma=1.5)
+    elif what == "multi-tile":
+        case = linear_case(24, 4, 70001, seed=32, dtype="bf16", noise_sigma=1.5)
+    else:
+        V, k = 64, 5
+        p = np.zeros((k + 1, V))
+        p[:, :32] = 1 / 32
+        q = np.zeros((k, V))
+        q[:, 32:] = 1 / 32
+        case = fixed_pq_case(p, q, 300, seed=3, dtype="bf16")
+    announce(f"workspace clean-up: {what} B={case.B} k={case.k} V={case.V}")
+    ws = sv.new_workspace(sv.SV_KIND_LINEAR, case.B, case.k, case.V)
+    ref = oracle_linear(case.logits, case.draft_probs, case.draft_tokens, 1.0, 9, 0)
+    for rep in range(2):
+        got = run_linear(case.logits, case.draft_probs, case.draft_tokens, 1.0, 9, 0, ws=ws)
+        assert int(ws.count_nonzero()) == 0, f"call {rep}: workspace not cleared"
+        check_linear(got, ref, case.logits.dtype, X=case.draft_tokens.numpy(), V=case.V,
+                     what=f"{what} call {rep}")
+    assert (ref["accept_len"] < case.k).sum() > 0  # the case has rejections
+
+
 def test_chisquare_gpu_output_law():
     """1e6 sequences, V = 8: tokens emitted at each reached position follow p_j."""
     rng = np.random.default_rng(31)
