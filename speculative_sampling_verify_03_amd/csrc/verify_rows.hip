@@ -84,10 +84,12 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   float* s_pm = s_dyn;
   float* s_ps = s_dyn + nunits;
   float* s_tot = s_dyn + 2 * nunits;
-  __shared__ int s_flag, s_y, s_last;
+  __shared__ int s_flag, s_y, s_last, s_skip;
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
   constexpr bool LOSSLESS = TREE && QMODE == kQLossless;
+  // single-tile linear rows with q vectors in phase: the rejection check is deferred (below)
+  constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
   __shared__ int s_xtok[LOSSLESS ? 64 : 1];  // lossless: the children's valid tokens
   __shared__ int s_nx;
 
@@ -272,11 +274,22 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     // an earlier rejection, so skipping changes no result.  At B=64, k=5, V=32000 this
     // cut the draws per step from ~149 to ~82 and the step from 20.8 to 18.7 us: a later
     // rejected row's draw no longer ends the step when an earlier row has rejected.
+    // A single-tile row reads the answer only at the barrier before its unit walk, so the
+    // atomic's round trip overlaps its draft-row loads and residual weights; a multi-tile
+    // row, whose draw re-reads its tiles, reads it before starting.
     {
       if (rejected) {
-        const uint64_t seen = atomic_max_u64(&P.seqword[2 * b + 1], static_cast<uint64_t>(64 - j));
-        rej_dep = seen;  // waited on before the ticket, so the reset cannot race it
-        if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+        if (DEFER) {
+          // a per-lane (opaque) address keeps the compiler from turning this into a
+          // one-lane atomic plus a broadcast, which would wait for the result at once
+          int zero;
+          asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+          rej_dep = atomic_max_u64(&P.seqword[2 * b + 1 + zero], static_cast<uint64_t>(64 - j));
+        } else {
+          const uint64_t seen = atomic_max_u64(&P.seqword[2 * b + 1], static_cast<uint64_t>(64 - j));
+          rej_dep = seen;  // waited on before the ticket, so the reset cannot race it
+          if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+        }
       } else if (cand) {  // the last row: any rejection makes it irrelevant
         const uint64_t seen =
             __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -293,6 +306,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     }
     s_usmp = us;
     s_y = -1;
+    s_skip = 0;
   }
   __syncthreads();
 
@@ -446,7 +460,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       // of every tile (residual draws only; the register-resident tile first, the others
       // re-read, mostly from cache); the last step locates the winning (tile, wave) and lets
       // that wave recompute its sums when they are not in registers already.
-      bool empty = false;
+      bool empty = false, skip = false;
       double t = 0.0, before = 0.0;
       bool clamp = false;
       int tile_s = 0, wave_s = 0;
@@ -465,7 +479,19 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           tile = (first + step) % P.ntiles;
           active = resid || (masked && unit_has_child(tile * NW + wid));
         } else {
+          // a single-tile rejected row's deferred check: an earlier rejection posted
+          // meanwhile makes this draw irrelevant
+          if (DEFER && resid && tid == 0) {
+            uint64_t seen = rej_dep;
+            asm volatile("" : "+v"(seen));  // the value is first needed here, not earlier
+            s_skip = seen > static_cast<uint64_t>(64 - j) ? 1 : 0;
+          }
           if (resid || masked) __syncthreads();
+          if (DEFER && s_skip) {
+            if (tid == 0) s_flag = 0;  // read again only by thread 0, when publishing
+            skip = true;
+            break;
+          }
           // weight of each (tile, wave) unit: the residual totals, or for a draw from p
           // itself the pass-1 partials rescaled to the row max (nothing recomputed)
           auto unit = [&](int q) -> float {
@@ -513,6 +539,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           if (step < P.ntiles && lane == 0) s_tot[tile * NW + wid] = wt;
         }
       }
+      if (DEFER && skip) break;
       if (empty) {
         if (!resid && !masked) break;
         resid = false;
