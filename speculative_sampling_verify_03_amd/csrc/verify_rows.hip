@@ -90,6 +90,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   constexpr bool LOSSLESS = TREE && QMODE == kQLossless;
   // single-tile linear rows with q vectors in phase: the rejection check is deferred (below)
   constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
+  // linear rows of several waves draw their position's pair in uniform control flow (below)
+  constexpr bool UNIFORM_RNG = !TREE && NT >= 256;
   __shared__ int s_xtok[LOSSLESS ? 64 : 1];  // lossless: the children's valid tokens
   __shared__ int s_nx;
 
@@ -166,6 +168,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     // every load of the tile is in flight before the first edge mask
     if (!PIPE) load_tile(buf, tile);
     else if (tile + 1 < P.ntiles) load_tile(nxt, tile + 1);
+    // Linear rows of several waves: the pair of position j is the same for every thread,
+    // so every thread draws it in uniform control flow (scalar instructions) while the
+    // tile's loads are in flight, instead of one lane of wave 0 spending some 300 vector
+    // issue slots on it inside pass 1 while the merge barrier waits for that wave
+    // (B=64 k=5 V=32000: 18.3 -> 17.7 us).  A one-wave workgroup has no barrier to shorten
+    // and measured slower this way (B=1000 k=4 V=1024: 13.3 -> 13.9 us), so it keeps the
+    // one-lane draw.
+    if (UNIFORM_RNG && tile == 0)
+      draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(j), g_uacc, g_usmp);
 #pragma unroll
     for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
     if (tile == 0 && g_node >= 0) {
@@ -174,7 +185,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         g_l = load_elem(rowp, g_x, BF16);
         if (!LOSSLESS) g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
       }
-      draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
+      if (!UNIFORM_RNG)
+        draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
     }
     float tm = -INFINITY;
 #pragma unroll
@@ -299,8 +311,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     s_flag = cand;
   }
   if (tid == 0) {
-    float us = g_usmp;  // linear: thread 0 drew the pair of position j
-    if (TREE || g_node < 0) {
+    float us = g_usmp;  // linear: the pair of position j (drawn above for rows j < k)
+    if (TREE || (!UNIFORM_RNG && g_node < 0)) {
       float ua;
       draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(j), ua, us);
     }
