@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParam
     for (int i0 = tid; i0 < n; i0 += NT * U) {
       Vec16 t[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) t[u] = ld16(pp, i0 + u * NT, n);
+      for (int u = 0; u < U; ++u) t[u] = ld16_stream(pp, i0 + u * NT, n);  // i >= n: unused below
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * NT;

@@ -160,7 +160,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   auto load_tile = [&](Vec16* dst, int tile) {
     const int v0 = tile * TILE + wid * (NV * kWave) + lane;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) dst[i] = ld16_any(vrow, v0 + i * kWave, nvec);  // edges: mask_edges
+    for (int i = 0; i < NV; ++i) dst[i] = ld16_stream(vrow, v0 + i * kWave, nvec);  // edges: mask_edges
   };
   if (PIPE) load_tile(buf, 0);
   for (int tile = 0; tile < P.ntiles; ++tile) {
