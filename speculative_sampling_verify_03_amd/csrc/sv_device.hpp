@@ -62,8 +62,8 @@ __device__ __forceinline__ Vec16 ld16(const SV_GLOBAL Vec16* p, int i, int n) {
 
 // 16-byte load of vector i when 0 <= i < n, else of vector 0 (n >= 1), with no select on the
 // result: for logits rows, mask_edges below turns every element of a vector past the row
-// into -inf anyway.  Loads with no consumer inside a conditional block (the next tile's
-// prefetch) then carry no wait with them.
+// into -inf anyway.  Loads with no consumer inside a conditional block (a tile's prefetch)
+// then carry no wait with them.  Used where a draw re-reads a tile of its row.
 __device__ __forceinline__ Vec16 ld16_any(const SV_GLOBAL Vec16* p, int i, int n) {
   const SV_GLOBAL Vec16& g = p[static_cast<unsigned>(i) < static_cast<unsigned>(n) ? i : 0];
   Vec16 v;
@@ -75,7 +75,7 @@ __device__ __forceinline__ Vec16 ld16_any(const SV_GLOBAL Vec16* p, int i, int n
 }
 
 // ld16_any as a non-temporal (streaming) load, for bytes that are read once: the logits of
-// a row's first pass and of the greedy scan.  Measured on MI355X: greedy B=256 k=8
+// a row's first pass (its tiles and their prefetch) and of the greedy scan.  Measured on MI355X: greedy B=256 k=8
 // V=128256 115 -> 104 us, linear B=64 k=5 V=32000 17.9 -> 17.1 us, B=256 k=8 141 -> 136 us.
 __device__ __forceinline__ Vec16 ld16_stream(const SV_GLOBAL Vec16* p, int i, int n) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
