@@ -35,6 +35,7 @@ from .verify import (  # noqa: F401
     verify_tree,
     lmhead_logits,
     lmhead_gemm_error_bound,
+    lmhead_gemm_error_bound_probabilistic,
     verify_lmhead,
 )
 from .plug import plug_tokens  # noqa: F401

@@ -32,13 +32,14 @@ from __future__ import annotations
 
 import numpy as np
 
-from .philox import uniforms
-from .verify import NEAR_TIE, inverse_cdf_sample, target_distribution, tree_depths
+from .verify import NEAR_TIE, _draws, inverse_cdf_sample, target_distribution, tree_depths
 
 
-def verify_tree_lossless(logits, node_tokens, parents, temperature: float, seed: int, offset: int = 0):
+def verify_tree_lossless(logits, node_tokens, parents, temperature: float, seed: int, offset: int = 0,
+                         seq_base: int = 0, u_shift=(0.0, 0.0)):
     """logits [B, N, V] (row u: target distribution after the path to node u), node_tokens
-    [B, N] (entry 0 unused), parents [N] (BFS order, parents[0] = -1).
+    [B, N] (entry 0 unused), parents [N] (BFS order, parents[0] = -1).  Sequence b draws
+    with sequence id seq_base + b; u_shift moves every draw (a test hook, default none).
     Returns tokens [B, D+1], path [B, D+1] (node ids, -1 padded), accept_len [B],
     chosen [B], acc_margin / smp_margin / near_tie [B], fallback [B]."""
     L = np.asarray(logits, dtype=np.float64)
@@ -67,7 +68,7 @@ def verify_tree_lossless(logits, node_tokens, parents, temperature: float, seed:
             nxt = -1
             for c in children[u]:
                 x = int(X[b, c])
-                u_acc, _ = uniforms(seed, b, c, offset)
+                u_acc, _ = _draws(seed, seq_base + b, c, offset, u_shift)
                 if not (0 <= x < V) or x in removed:
                     continue      # rejected; removes nothing new
                 W = 1.0 - before
@@ -90,7 +91,7 @@ def verify_tree_lossless(logits, node_tokens, parents, temperature: float, seed:
         if np.sum(w) == 0.0:
             w = p
             out["fallback"][b] = True
-        _, u_smp = uniforms(seed, b, u, offset)
+        _, u_smp = _draws(seed, seq_base + b, u, offset, u_shift)
         y, smargin = inverse_cdf_sample(w, u_smp)
         d = len(path) - 1
         out["chosen"][b] = u

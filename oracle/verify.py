@@ -48,6 +48,17 @@ from .philox import uniforms
 NEAR_TIE = 1e-6
 
 
+def _draws(seed: int, seq: int, pos: int, offset: int, u_shift=(0.0, 0.0)):
+    """(u_acc, u_smp) of one position, each moved by u_shift and kept inside [0, 1).
+
+    u_shift is a test hook (default: no shift): moving every draw of a sequence by about
+    the near-tie width shows which outcomes a near-tie decision can take.
+    """
+    u_acc, u_smp = uniforms(seed, seq, pos, offset)
+    top = 1.0 - 2.0 ** -53
+    return (min(max(u_acc + u_shift[0], 0.0), top), min(max(u_smp + u_shift[1], 0.0), top))
+
+
 def target_distribution(logit_row, temperature: float) -> np.ndarray:
     """p = softmax(l / T) over one vocabulary row, float64."""
     z = np.asarray(logit_row, dtype=np.float64) / float(temperature)
@@ -93,16 +104,19 @@ def _accept(u_acc: float, px: float, qx: float):
 
 
 def verify_linear(logits, draft_probs, draft_tokens, temperature: float, seed: int,
-                  offset: int = 0):
+                  offset: int = 0, seq_base: int = 0, u_shift=(0.0, 0.0)):
     """Linear speculative sampling.
 
-    logits [B, k+1, V], draft_probs [B, k, V], draft_tokens [B, k] int.
+    logits [B, k+1, V], draft_probs [B, k, V], draft_tokens [B, k] int.  Sequence b
+    draws with sequence id seq_base + b (seq_base lets a caller verify one sequence of a
+    batch on its own); u_shift is the test hook of _draws.
     Returns a dict of numpy arrays:
       tokens [B, k+1] (emitted tokens, -1 padded), accept_len [B] (= n, drafts kept;
       emitted = n + 1), target_prob [B, k] (p_j(x_j)), accept_prob [B, k]
       (min(1, p/q)), accepted [B, k] (every position's test), fallback [B] (S = 0 path),
-      acc_margin / smp_margin [B] (distance of the deciding draws from their
-      thresholds) and near_tie [B] (either margin below 1e-6).
+      residual_mass [B] (S of the final draw's weights: the residual mass, or 1 for a
+      draw from p), acc_margin / smp_margin [B] (distance of the deciding draws from
+      their thresholds) and near_tie [B] (either margin below 1e-6).
     """
     L = np.asarray(logits, dtype=np.float64)
     Q = np.asarray(draft_probs, dtype=np.float64)
@@ -116,6 +130,7 @@ def verify_linear(logits, draft_probs, draft_tokens, temperature: float, seed: i
         accept_prob=np.zeros((B, k), dtype=np.float64),
         accepted=np.zeros((B, k), dtype=bool),
         fallback=np.zeros(B, dtype=bool),
+        residual_mass=np.ones(B, dtype=np.float64),
         acc_margin=np.full(B, np.inf),
         smp_margin=np.full(B, np.inf),
     )
@@ -123,7 +138,7 @@ def verify_linear(logits, draft_probs, draft_tokens, temperature: float, seed: i
         p = [target_distribution(L[b, j], temperature) for j in range(R)]
         n = k
         for j in range(k):
-            u_acc, _ = uniforms(seed, b, j, offset)
+            u_acc, _ = _draws(seed, seq_base + b, j, offset, u_shift)
             x = int(X[b, j])
             if 0 <= x < V:
                 acc, margin, aprob = _accept(u_acc, p[j][x], Q[b, j, x])
@@ -136,12 +151,14 @@ def verify_linear(logits, draft_probs, draft_tokens, temperature: float, seed: i
                 out["acc_margin"][b] = min(out["acc_margin"][b], margin)
                 if not acc:
                     n = j
-        _, u_smp = uniforms(seed, b, n, offset)
+        _, u_smp = _draws(seed, seq_base + b, n, offset, u_shift)
         if n < k:
             w = np.maximum(0.0, p[n] - Q[b, n])
             if np.sum(w) == 0.0:
                 w = p[n]
                 out["fallback"][b] = True
+            else:
+                out["residual_mass"][b] = np.sum(w)
         else:
             w = p[k]
         y, smargin = inverse_cdf_sample(w, u_smp)
@@ -187,7 +204,7 @@ def tree_depths(parents) -> np.ndarray:
 
 
 def verify_tree(logits, draft_probs, node_tokens, parents, temperature: float, seed: int,
-                offset: int = 0):
+                offset: int = 0, seq_base: int = 0, u_shift=(0.0, 0.0)):
     """Static-tree verification.
 
     logits [B, N, V] (row u: target distribution after the path to node u),
@@ -196,7 +213,8 @@ def verify_tree(logits, draft_probs, node_tokens, parents, temperature: float, s
     = -1, 0 <= parents[c] < c).
     Returns tokens [B, D+1] and path [B, D+1] (node ids root..chosen, -1 padded) with D
     the tree depth, accept_len [B] (depth of the chosen node), chosen [B], accepted and
-    alive [B, N], acc_margin / smp_margin / near_tie [B].
+    alive [B, N], acc_margin / smp_margin / near_tie [B].  seq_base and u_shift: as for
+    verify_linear.
     """
     L = np.asarray(logits, dtype=np.float64)
     Q = np.asarray(draft_probs, dtype=np.float64)
@@ -229,7 +247,7 @@ def verify_tree(logits, draft_probs, node_tokens, parents, temperature: float, s
         for c in range(1, N):
             u = int(par[c])
             x = int(T_[b, c])
-            u_acc, _ = uniforms(seed, b, c, offset)
+            u_acc, _ = _draws(seed, seq_base + b, c, offset, u_shift)
             if 0 <= x < V:
                 acc, margin, _ = _accept(u_acc, prow(u)[x], Q[b, u, x])
             else:
@@ -247,7 +265,7 @@ def verify_tree(logits, draft_probs, node_tokens, parents, temperature: float, s
         while chain[-1] != 0:
             chain.append(int(par[chain[-1]]))
         chain.reverse()
-        _, u_smp = uniforms(seed, b, best, offset)
+        _, u_smp = _draws(seed, seq_base + b, best, offset, u_shift)
         y, smargin = inverse_cdf_sample(prow(best), u_smp)
         d = int(depth[best])
         out["chosen"][b] = best
@@ -285,6 +303,27 @@ def lmhead_gemm_error_bound(hidden, weight) -> np.ndarray:
     u = 2.0 ** -24
     gamma = K * u / (1.0 - K * u)
     return 2.0 * gamma * (h @ w)
+
+
+def lmhead_gemm_error_bound_probabilistic(hidden, weight, lam: float = 10.0) -> np.ndarray:
+    """Entrywise probabilistic bound on |fp32-accumulated hidden @ W - exact|.
+
+    Higham and Mary, "A new approach to probabilistic rounding error analysis" (SIAM J.
+    Sci. Comput. 41(5), 2019): if the rounding errors of the K additions are independent,
+    mean-zero and at most u in size, the computed inner product is within
+    gamma(lam) * sum_h |a_h w_hv| of the exact one, gamma(lam) = exp(lam sqrt(K) u +
+    K u^2 / (1 - u)) - 1, except with probability at most 2 K exp(-lam^2 (1 - u)^2 / 2).
+    lam = 10 at K = 8192: at most 3.1e-18 per entry; the bound is about 1/18 of the
+    worst-case one (lmhead_gemm_error_bound) there, tight enough that leaving out one
+    product a_h * w_hv of typical size exceeds it.  Products of bf16 values are exact in
+    float32, so only the additions round.
+    """
+    h = np.abs(np.asarray(hidden, dtype=np.float64))
+    w = np.abs(np.asarray(weight, dtype=np.float64))
+    K = h.shape[-1]
+    u = 2.0 ** -24
+    gamma = np.expm1(lam * np.sqrt(K) * u + K * u * u / (1.0 - u))
+    return gamma * (h @ w)
 
 
 def verify_lmhead(hidden, weight, draft_probs, draft_tokens, temperature: float,

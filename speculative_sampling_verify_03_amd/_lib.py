@@ -111,6 +111,22 @@ def _f32(t, shape, name):
     return _ptr(t)
 
 
+def _tree_width(parents, B, out_tokens, out_path):
+    """D + 1 for a parent array (D = depth of its deepest node), checked against the
+    output buffers: the kernels write exactly B * (D + 1) entries with that row stride."""
+    depth = [0] * len(parents)
+    for c in range(1, len(parents)):
+        p = int(parents[c])
+        if not 0 <= p < c:
+            raise ValueError("parents must satisfy 0 <= parents[c] < c for c >= 1")
+        depth[c] = depth[p] + 1
+    W = max(depth) + 1 if depth else 1
+    for name, t in (("out_tokens", out_tokens), ("out_path", out_path)):
+        if t is not None and tuple(t.shape) != (B, W):
+            raise ValueError(f"{name} must have shape {(B, W)} for this tree, got {tuple(t.shape)}")
+    return W
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -195,13 +211,15 @@ def spec_verify_tree(target_logits, draft_probs, node_tokens, parents, temperatu
     """target_logits / draft_probs [B, N, V]; node_tokens int32 [B, N]; parents: host
     sequence of N ints (BFS order, parents[0] = -1); outputs [B, D+1], [B], [B, D+1]."""
     B, N, V = target_logits.shape
+    if len(parents) != N:
+        raise ValueError(f"parents must have N = {N} entries")
     par = (ctypes.c_int32 * N)(*[int(x) for x in parents])
-    D = out_tokens.shape[1] - 1
+    W = _tree_width(parents, B, out_tokens, out_path)
     rc = _lib().spec_verify_tree(
         _ptr(target_logits), _dt(target_logits), _ptr(draft_probs), _dt(draft_probs),
         _i32(node_tokens, (B, N), "node_tokens"), ctypes.cast(par, ctypes.c_void_p), B, N, V,
-        float(temperature), int(seed), int(offset), _i32(out_tokens, (B, D + 1), "out_tokens"),
-        _i32(out_accept_len, (B,), "out_accept_len"), _i32(out_path, (B, D + 1), "out_path"),
+        float(temperature), int(seed), int(offset), _i32(out_tokens, (B, W), "out_tokens"),
+        _i32(out_accept_len, (B,), "out_accept_len"), _i32(out_path, (B, W), "out_path"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_verify_tree")
 
@@ -212,13 +230,15 @@ def spec_verify_tree_lossless(target_logits, node_tokens, parents, temperature, 
     (BFS order, parents[0] = -1); outputs [B, D+1], [B], [B, D+1].  No draft
     probabilities: each node's token is a fixed top-K candidate."""
     B, N, V = target_logits.shape
+    if len(parents) != N:
+        raise ValueError(f"parents must have N = {N} entries")
     par = (ctypes.c_int32 * N)(*[int(x) for x in parents])
-    D = out_tokens.shape[1] - 1
+    W = _tree_width(parents, B, out_tokens, out_path)
     rc = _lib().spec_verify_tree_lossless(
         _ptr(target_logits), _dt(target_logits), _i32(node_tokens, (B, N), "node_tokens"),
         ctypes.cast(par, ctypes.c_void_p), B, N, V, float(temperature), int(seed), int(offset),
-        _i32(out_tokens, (B, D + 1), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"),
-        _i32(out_path, (B, D + 1), "out_path"),
+        _i32(out_tokens, (B, W), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"),
+        _i32(out_path, (B, W), "out_path"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_verify_tree_lossless")
 

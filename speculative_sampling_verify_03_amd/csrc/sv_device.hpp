@@ -306,8 +306,11 @@ __device__ __forceinline__ void reset_ticket(uint32_t* counter) {
 __device__ __forceinline__ void after_value(uint64_t v) { asm volatile("" ::"v"(v) : "memory"); }
 
 // Orderable 64-bit key of an argmax candidate: larger value first, then lower index.
+// -0.0 is keyed as +0.0: the two compare equal, so between them the lower index must win,
+// as it does in the float comparisons of the in-thread and in-wave merges.
 __device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
-  const uint32_t u = __float_as_uint(v);
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0u) u = 0u;
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<uint64_t>(o) << 32) | (0xffffffffu - static_cast<uint32_t>(idx));
 }

@@ -2,9 +2,12 @@
 binding) on seeded inputs and compare with the CPU oracle.
 
 Bar: accepted lengths, emitted tokens and tree paths bit-exact, except sequences the
-oracle flags as near-ties (a deciding uniform within 1e-6 of its threshold; those are
-counted, and must stay rare); target probabilities and min(1, p/q) within 1e-5 for
-float32 inputs and 2e-3 for bfloat16 inputs.
+oracle flags as near-ties (a deciding uniform within 1e-6 of its threshold).  Near-ties
+are counted and reported (tests/tie_report.py, printed in the session summary); a
+near-tie sequence on which the GPU differs from the oracle must still give an outcome
+the oracle reaches on that sequence with its draws moved by at most 1e-6
+(explain_near_ties).  Target probabilities and min(1, p/q) within 1e-5 for float32
+inputs and 2e-3 for bfloat16 inputs.
 """
 from __future__ import annotations
 
@@ -12,8 +15,11 @@ import numpy as np
 import torch
 
 import speculative_sampling_verify_03_amd as sv
+import tie_report
 from oracle import verify_greedy, verify_linear, verify_tree
 from synthetic import to_numpy_f64
+
+NEAR = 1e-6
 
 DEV = "cuda"
 PROB_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-3}
@@ -53,7 +59,57 @@ def run_linear(logits, probs, tokens, T, seed, offset=0, misalign=(0, 0), ws=Non
 
 
 def oracle_linear(logits, probs, tokens, T, seed, offset=0):
-    return verify_linear(to_numpy_f64(logits), to_numpy_f64(probs), tokens.numpy(), T, seed, offset)
+    """The oracle's result, with ``rerun(b, shift)``: sequence b alone, draws shifted."""
+    return oracle_linear_f64(to_numpy_f64(logits), to_numpy_f64(probs), tokens.numpy(), T, seed, offset)
+
+
+def oracle_linear_f64(L, Q, X, T, seed, offset=0):
+    ref = verify_linear(L, Q, X, T, seed, offset)
+    ref["rerun"] = lambda b, sh: verify_linear(L[b:b + 1], Q[b:b + 1], X[b:b + 1], T, seed, offset,
+                                               seq_base=int(b), u_shift=sh)
+    return ref
+
+
+def explain_near_ties(got, ref, differ, what):
+    """Every near-tie sequence on which the GPU differs from the oracle must give an outcome
+    the oracle reaches on that sequence with its draws moved by at most 1e-6.  The
+    acceptance draws are moved by -1e-6, 0 or +1e-6 (they decide the accepted length and,
+    for a tree, the path); for each of those, the extra token is drawn by inverse CDF,
+    which is monotone in the sampling draw, so moving that draw anywhere in [-1e-6, +1e-6]
+    reaches exactly the tokens between the draws at the two ends.  Returns how many
+    sequences were explained this way."""
+    n_explained = 0
+    has_path = "path" in got
+    for b in np.nonzero(differ & ref["near_tie"])[0]:
+        seen = []
+        ok = False
+        for da in (-NEAR, 0.0, NEAR):
+            lo = ref["rerun"](b, (da, -NEAR))
+            hi = ref["rerun"](b, (da, NEAR))
+            n = int(lo["accept_len"][0])
+            assert int(hi["accept_len"][0]) == n  # the sampling draw does not move the length
+            seen.append((n, lo["tokens"][0].tolist(), hi["tokens"][0].tolist()))
+            if int(got["accept_len"][b]) != n:
+                continue
+            t = got["tokens"][b]
+            same = np.array_equal(t[:n], lo["tokens"][0, :n]) and np.all(t[n + 1:] == -1)
+            if has_path:
+                same = same and np.array_equal(got["path"][b], lo["path"][0])
+            if same and lo["tokens"][0, n] <= t[n] <= hi["tokens"][0, n]:
+                ok = True
+                break
+        assert ok, (f"{what}: near-tie sequence {b} gives length {got['accept_len'][b]} tokens "
+                    f"{got['tokens'][b].tolist()}, outside what draws within 1e-6 of the oracle's reach: {seen}")
+        n_explained += 1
+    return n_explained
+
+
+def report(what, ok, diff, explained):
+    ties = int((~ok).sum())
+    line = (f"{what}: {int(ok.sum())} of {ok.size} sequences bit-exact; {ties} near-ties excluded "
+            f"({int((~ok & ~diff).sum())} match anyway, {explained} differ within a 1e-6 shift of the draws)")
+    announce(line)
+    tie_report.add(line)
 
 
 def _valid_linear_rows(got, X, V):
@@ -83,18 +139,19 @@ def check_linear(got, ref, dtype, X=None, V=None, what=""):
                            f"gpu {got['tokens'][bad[:3]]} len {got['accept_len'][bad[:3]]} / "
                            f"oracle {ref['tokens'][bad[:3]]} len {ref['accept_len'][bad[:3]]}")
     ties = int((~ok).sum())
-    tie_match = int((~ok & ~diff).sum())
     if X is not None and ties:
         valid = _valid_linear_rows(got, X, V)
         assert np.all(valid[~ok]), f"{what}: malformed output on a near-tie sequence"
+    explained = explain_near_ties(got, ref, diff, what) if "rerun" in ref else 0
+    if "rerun" not in ref:
+        assert not np.any(diff & ~ok), f"{what}: near-tie mismatches and no way to rerun the oracle"
     tol = PROB_TOL[dtype]
     if got["target_prob"].size:
         e1 = np.abs(got["target_prob"] - ref["target_prob"]).max()
         e2 = np.abs(got["accept_prob"] - ref["accept_prob"]).max()
         assert e1 <= tol and e2 <= tol, f"{what}: probability error {e1:.3g} / {e2:.3g} > {tol}"
         announce(f"{what}: max |dp| {e1:.2g}, max |d min(1,p/q)| {e2:.2g}")
-    announce(f"{what}: {ok.sum()} of {ok.size} sequences bit-exact; {ties} near-ties excluded "
-             f"({tie_match} of them match anyway)")
+    report(what, ok, diff, explained)
     return ties
 
 
@@ -136,8 +193,10 @@ def run_tree(case, seed, offset=0, misalign=(0, 0)):
 
 
 def check_tree(got, case, seed, offset=0, what=""):
-    ref = verify_tree(to_numpy_f64(case.logits), to_numpy_f64(case.draft_probs), case.node_tokens.numpy(),
-                      case.parents, case.temperature, seed, offset)
+    L, Q, X = to_numpy_f64(case.logits), to_numpy_f64(case.draft_probs), case.node_tokens.numpy()
+    ref = verify_tree(L, Q, X, case.parents, case.temperature, seed, offset)
+    ref["rerun"] = lambda b, sh: verify_tree(L[b:b + 1], Q[b:b + 1], X[b:b + 1], case.parents, case.temperature,
+                                             seed, offset, seq_base=int(b), u_shift=sh)
     ok = ~ref["near_tie"]
     diff = ((got["accept_len"] != ref["accept_len"]) | np.any(got["tokens"] != ref["tokens"], axis=1)
             | np.any(got["path"] != ref["path"], axis=1))
@@ -154,8 +213,6 @@ def check_tree(got, case, seed, offset=0, what=""):
         assert path[0] == 0 and all(par[path[i]] == path[i - 1] for i in range(1, d + 1)), what
         assert list(got["tokens"][b, :d]) == [toks[b, c] for c in path[1:d + 1]], what
         assert 0 <= got["tokens"][b, d] < V and np.all(got["tokens"][b, d + 1:] == -1), what
-    ties = int((~ok).sum())
-    tie_match = int((~ok & ~diff).sum())
-    announce(f"{what}: {ok.sum()} of {ok.size} sequences bit-exact; {ties} near-ties excluded "
-             f"({tie_match} of them match anyway)")
+    explained = explain_near_ties(got, ref, diff, what)
+    report(what, ok, diff, explained)
     return ref

@@ -212,3 +212,32 @@ def test_lookup_validation_codes():
     assert lookup(k=65) == -2
     assert lookup(cap=0) == -2
     assert lookup(drafts=C(0x1001)) == -9
+
+
+@pytest.mark.parametrize("fn", ["spec_verify_tree", "spec_verify_tree_lossless"])
+@pytest.mark.parametrize("width", [1, 3, 5, 7])
+def test_tree_binding_rejects_wrong_output_width(fn, width):
+    """The tree kernels write B * (D + 1) entries with stride D + 1, D the tree's depth
+    (3 here).  The binding derives D + 1 from the parent array and refuses buffers of any
+    other width before anything reaches the library (CPU tensors never get that far)."""
+    B, N, V = 2, 5, 16
+    parents = [-1, 0, 0, 1, 3]  # depths 0, 1, 1, 2, 3
+    lg = torch.zeros((B, N, V))
+    toks = torch.zeros((B, N), dtype=torch.int32)
+    out = torch.zeros((B, width), dtype=torch.int32)
+    alen = torch.zeros((B,), dtype=torch.int32)
+    args = (lg, lg, toks, parents) if fn == "spec_verify_tree" else (lg, toks, parents)
+    with pytest.raises(ValueError, match="out_tokens must have shape"):
+        getattr(sv, fn)(*args, 1.0, 0, 0, out, alen)
+    good = torch.zeros((B, 4), dtype=torch.int32)
+    bad_path = torch.zeros((B, width), dtype=torch.int32)
+    with pytest.raises(ValueError, match="out_path must have shape"):
+        getattr(sv, fn)(*args, 1.0, 0, 0, good, alen, bad_path)
+
+
+def test_tree_binding_rejects_parent_count():
+    lg = torch.zeros((1, 3, 8))
+    with pytest.raises(ValueError, match="parents must have"):
+        sv.spec_verify_tree_lossless(lg, torch.zeros((1, 3), dtype=torch.int32), [-1, 0], 1.0, 0, 0,
+                                     torch.zeros((1, 2), dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+

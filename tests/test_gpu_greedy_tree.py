@@ -59,12 +59,39 @@ def test_greedy_ties_lowest_index():
     check_greedy(got, L, X, what="greedy ties")
 
 
-def test_cfg5_tree_full():
-    case = cfg5_case()
-    announce("tree B=16 N=61 V=128256 bf16")
+@pytest.mark.parametrize("case_seed", [5, 105, 205, 305])
+def test_cfg5_tree_full(case_seed):
+    # four generated batches of the page's tree: 64 sequences at full size
+    announce(f"tree B=16 N=61 V=128256 bf16, inputs seed {case_seed} (generating)")
+    case = cfg5_case(seed=case_seed)
     got = run_tree(case, seed=0)
-    ref = check_tree(got, case, seed=0, what="tree B=16 N=61 V=128256")
+    ref = check_tree(got, case, seed=0, what=f"tree B=16 N=61 V=128256 inputs {case_seed}")
     announce(f"tree mean accept_len {ref['accept_len'].mean():.3f}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_greedy_signed_zero_maximum(dtype, misalign):
+    """Rows whose maximum is zero, held as -0.0 in one piece of the row and +0.0 in a
+    later one (rows of 128256 are cut into several workgroups' pieces on both the flat
+    path, misalign 0, and the split path, misalign 1).  The two compare equal, so the
+    lower index wins whichever sign it carries."""
+    V = 128256
+    L = torch.full((2, 3, V), -1.0, dtype=dtype)
+    L[0, 0, 5] = -0.0
+    L[0, 0, 100000] = 0.0     # later piece, +0.0
+    L[0, 1, 9] = 0.0
+    L[0, 1, 90000] = -0.0     # later piece, -0.0
+    L[0, 2, 64000] = -0.0
+    L[0, 2, 127999] = 0.0
+    L[1, :, 70000] = -0.0
+    L[1, :, 120000] = 0.0
+    X = torch.tensor([[5, 9], [70000, 120000]], dtype=torch.int32)
+    assert int(L[0, 0, 5].view(torch.int16 if dtype == torch.bfloat16 else torch.int32)) < 0  # really -0.0
+    got = run_greedy(L, X, misalign)
+    assert list(got["accept_len"]) == [2, 1]
+    assert list(got["tokens"][0]) == [5, 9, 64000] and list(got["tokens"][1]) == [70000, 70000, -1]
+    check_greedy(got, L, X, what=f"greedy signed zero {dtype} misalign={misalign}")
 
 
 @pytest.mark.parametrize("name", ["chain", "single", "wide", "deep64"])

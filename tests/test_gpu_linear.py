@@ -6,6 +6,7 @@ import torch
 from scipy import stats
 
 from gpu_common import announce, check_linear, oracle_linear, run_linear
+from oracle import verify_linear
 from synthetic import cfg1_case, cfg2_case, cfg3_case, fixed_pq_case, linear_case, mtp_case, to_numpy_f64
 
 pytestmark = pytest.mark.gpu
@@ -26,14 +27,31 @@ def test_cfg1_batched_1000():
 
 
 def test_cfg1_sequential_steps():
-    case = cfg1_case(B=100)
-    for s in range(100):
-        lg = case.logits[s:s + 1]
-        q = case.draft_probs[s:s + 1]
-        x = case.draft_tokens[s:s + 1]
-        got = run_linear(lg, q, x, 1.0, 0, s)
-        ref = oracle_linear(lg, q, x, 1.0, 0, s)
-        check_linear(got, ref, torch.float32, what=f"B=1 k=4 V=1024 step {s}")
+    """The B=1, k=4, V=1024 float32 workload as stated: 1000 independent verify calls of
+    one sequence, Philox seed 0, step s drawing with offset s, one workspace reused."""
+    import speculative_sampling_verify_03_amd as sv
+    steps = 1000
+    case = cfg1_case(B=steps)
+    announce(f"B=1 k=4 V=1024 f32: {steps} sequential calls")
+    lg, q, x = case.logits.to("cuda"), case.draft_probs.to("cuda"), case.draft_tokens.to("cuda")
+    toks = torch.full((steps, 5), -7, dtype=torch.int32, device="cuda")
+    alen = torch.full((steps,), -7, dtype=torch.int32, device="cuda")
+    tp = torch.full((steps, 4), -7.0, dtype=torch.float32, device="cuda")
+    ap = torch.full((steps, 4), -7.0, dtype=torch.float32, device="cuda")
+    ws = sv.new_workspace(sv.SV_KIND_LINEAR, 1, 4, 1024)
+    for s in range(steps):
+        sv.spec_verify_linear(lg[s:s + 1], q[s:s + 1], x[s:s + 1], 1.0, 0, s, toks[s:s + 1], alen[s:s + 1],
+                              tp[s:s + 1], ap[s:s + 1], ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    got = dict(tokens=toks.cpu().numpy(), accept_len=alen.cpu().numpy(), target_prob=tp.cpu().numpy(),
+               accept_prob=ap.cpu().numpy())
+    L, Q, X = to_numpy_f64(case.logits), to_numpy_f64(case.draft_probs), case.draft_tokens.numpy()
+    refs = [verify_linear(L[s:s + 1], Q[s:s + 1], X[s:s + 1], 1.0, 0, s) for s in range(steps)]
+    ref = {key: np.concatenate([r[key] for r in refs]) for key in refs[0]}
+    ref["rerun"] = lambda s, sh: verify_linear(L[s:s + 1], Q[s:s + 1], X[s:s + 1], 1.0, 0, int(s), u_shift=sh)
+    check_linear(got, ref, torch.float32, X=X, V=1024, what=f"B=1 k=4 V=1024 f32, {steps} sequential steps")
+    announce(f"sequential steps: mean emitted {ref['accept_len'].mean() + 1:.3f}")
 
 
 def test_cfg2_full():

@@ -9,7 +9,7 @@ import torch
 from scipy import stats
 
 import speculative_sampling_verify_03_amd as sv
-from gpu_common import announce, on_device
+from gpu_common import announce, explain_near_ties, on_device, report
 from oracle import target_distribution, verify_tree_lossless
 from synthetic import cfg5_case, chain_tree_parents, eagle_tree_parents, to_numpy_f64, tree_case
 
@@ -35,7 +35,10 @@ def run(logits, node_tokens, parents, T, seed, offset=0, misalign=0):
 
 
 def check(got, logits, node_tokens, parents, T, seed, offset=0, what=""):
-    ref = verify_tree_lossless(to_numpy_f64(logits), node_tokens.numpy(), parents, T, seed, offset)
+    L, X = to_numpy_f64(logits), node_tokens.numpy()
+    ref = verify_tree_lossless(L, X, parents, T, seed, offset)
+    ref["rerun"] = lambda b, sh: verify_tree_lossless(L[b:b + 1], X[b:b + 1], parents, T, seed, offset,
+                                                      seq_base=int(b), u_shift=sh)
     ok = ~ref["near_tie"]
     diff = ((got["accept_len"] != ref["accept_len"]) | np.any(got["tokens"] != ref["tokens"], axis=1)
             | np.any(got["path"] != ref["path"], axis=1))
@@ -44,10 +47,9 @@ def check(got, logits, node_tokens, parents, T, seed, offset=0, what=""):
                            f"{got['path'][bad[:2]]} / oracle {ref['tokens'][bad[:2]]} {ref['path'][bad[:2]]}")
     # near-ties are mostly draws: with V in the thousands the CDF steps are 1e-4 apart or
     # less, so a uniform lands within 1e-6 of one in a few percent of sequences
-    ties = int((~ok).sum())
-    announce(f"{what}: {ok.sum()} of {ok.size} bit-exact, {ties} near-ties excluded "
-             f"({int((~ok & ~diff).sum())} match anyway), mean accept_len {ref['accept_len'].mean():.3f}, "
-             f"{int(ref['fallback'].sum())} fallbacks")
+    explained = explain_near_ties(got, ref, diff, what)
+    report(what, ok, diff, explained)
+    announce(f"{what}: mean accept_len {ref['accept_len'].mean():.3f}, {int(ref['fallback'].sum())} fallbacks")
     return ref
 
 

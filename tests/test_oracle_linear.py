@@ -299,3 +299,48 @@ def test_offset_changes_draws_and_is_reproducible():
     c = _run(case, seed=1, offset=1)
     assert np.array_equal(a["tokens"], b["tokens"])
     assert not np.array_equal(a["tokens"], c["tokens"])
+
+
+def test_seq_base_verifies_one_sequence_of_a_batch():
+    """Sequence b of a batch, verified on its own with seq_base = b, gives the batch's row b."""
+    case = linear_case(6, 3, 40, seed=12, dtype="f32", noise_sigma=1.0)
+    L, Q, X = to_numpy_f64(case.logits), to_numpy_f64(case.draft_probs), case.draft_tokens.numpy()
+    full = verify_linear(L, Q, X, 1.0, seed=4, offset=2)
+    for b in range(6):
+        one = verify_linear(L[b:b + 1], Q[b:b + 1], X[b:b + 1], 1.0, seed=4, offset=2, seq_base=b)
+        assert np.array_equal(one["tokens"][0], full["tokens"][b])
+        assert one["accept_len"][0] == full["accept_len"][b]
+
+
+def test_u_shift_moves_a_near_tie_decision():
+    """The u_shift hook: with p/q set to the position's own u_acc plus 5e-7, the test
+    accepts; moving u_acc up by 1e-6 rejects it.  A zero shift changes nothing."""
+    from oracle import uniforms
+    V = 4
+    u_acc, _ = uniforms(3, 0, 0, 0)
+    q = np.array([[[0.25, 0.25, 0.25, 0.25]]])
+    ratio = u_acc + 5e-7
+    p0 = ratio * 0.25
+    rest = (1.0 - p0) / 3.0
+    L = np.log(np.array([[[p0, rest, rest, rest], [0.25, 0.25, 0.25, 0.25]]]))
+    X = np.array([[0]])
+    base = verify_linear(L, q, X, 1.0, seed=3)
+    assert base["accept_len"][0] == 1 and base["near_tie"][0]
+    assert np.array_equal(verify_linear(L, q, X, 1.0, seed=3, u_shift=(0.0, 0.0))["tokens"], base["tokens"])
+    up = verify_linear(L, q, X, 1.0, seed=3, u_shift=(1e-6, 0.0))
+    assert up["accept_len"][0] == 0
+    assert V == L.shape[-1]
+
+
+def test_residual_mass_is_reported():
+    """residual_mass is sum max(0, p_n - q_n) after a rejection and 1 after a full accept."""
+    case = linear_case(16, 2, 30, seed=13, dtype="f32", noise_sigma=1.5)
+    L, Q, X = to_numpy_f64(case.logits), to_numpy_f64(case.draft_probs), case.draft_tokens.numpy()
+    out = verify_linear(L, Q, X, 1.0, seed=1)
+    for b in range(16):
+        n = out["accept_len"][b]
+        if n < 2 and not out["fallback"][b]:
+            p = target_distribution(L[b, n], 1.0)
+            assert np.isclose(out["residual_mass"][b], np.maximum(0.0, p - Q[b, n]).sum(), rtol=1e-12)
+        else:
+            assert out["residual_mass"][b] == 1.0
