@@ -72,7 +72,8 @@ enum {
   SV_E_WORKSPACE = -6,  /* workspace NULL or smaller than required                      */
   SV_E_DEVICE = -7,     /* current HIP device is not gfx950                             */
   SV_E_LAUNCH = -8,     /* the HIP runtime refused a kernel launch                      */
-  SV_E_ALIGN = -9       /* a tensor pointer is not aligned to its element size          */
+  SV_E_ALIGN = -9,      /* a tensor pointer is not aligned to its element size          */
+  SV_E_SCRATCH = -10    /* sizes need more than the static scratch of the _noalloc call */
 };
 
 enum { SV_KIND_LINEAR = 0, SV_KIND_GREEDY = 1, SV_KIND_TREE = 2, SV_KIND_LMHEAD = 3 };
@@ -99,6 +100,24 @@ SV_API int spec_verify_linear(const void* target_logits, int lt, const void* dra
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_target_prob, float* out_accept_prob,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_linear without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as spec_verify_linear, minus the workspace: the
+ * per-sequence and per-row words live in a static device array of 1 MiB that the library
+ * holds on every device it runs on until the process ends.  Each call clears the part it
+ * uses (one small fill kernel on `stream`) and allocates nothing.  Every call on one
+ * device shares that array, so calls that may overlap on one device (concurrent streams,
+ * several host threads) race and must be serialised by the caller.
+ * Returns SV_E_SCRATCH when spec_verify_workspace_bytes(SV_KIND_LINEAR, B, k, V, 0) exceeds
+ * 1 MiB, decided before any device call.
+ */
+SV_API int spec_verify_linear_noalloc(const void* target_logits, int lt, const void* draft_probs, int qt,
+                       const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V,
+                       float temperature, uint64_t seed, uint64_t offset,
+                       int32_t* out_tokens, int32_t* out_accept_len,
+                       float* out_target_prob, float* out_accept_prob, void* stream);
 
 /*
  * Greedy verification: draft token j is kept while it equals the argmax of target row j

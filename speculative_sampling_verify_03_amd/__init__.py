@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     library,
     new_workspace,
     spec_lmhead_verify,
+    spec_verify_linear_noalloc,
     spec_lookup_drafts,
     spec_plug_tokens,
     spec_verify_greedy,

@@ -22,8 +22,9 @@ SV_KIND_LINEAR, SV_KIND_GREEDY, SV_KIND_TREE, SV_KIND_LMHEAD = 0, 1, 2, 3
 ERRORS = {
     0: "SV_OK", -1: "SV_E_NULL", -2: "SV_E_SHAPE", -3: "SV_E_DTYPE", -4: "SV_E_TEMP",
     -5: "SV_E_TREE", -6: "SV_E_WORKSPACE", -7: "SV_E_DEVICE", -8: "SV_E_LAUNCH", -9: "SV_E_ALIGN",
+    -10: "SV_E_SCRATCH",
 }
-EXPORTS = ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
+EXPORTS = ("spec_verify_linear", "spec_verify_linear_noalloc", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
            "spec_lmhead_verify",
            "spec_plug_tokens", "spec_lookup_drafts", "spec_verify_workspace_bytes", "spec_verify_strerror")
 
@@ -51,6 +52,8 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         lib.spec_verify_linear.argtypes = [_P, ctypes.c_int, _P, ctypes.c_int, _P, _I32, _I32, _I32, _F32,
                                            _U64, _U64, _P, _P, _P, _P, _P, _SZ, _P]
+        lib.spec_verify_linear_noalloc.argtypes = [_P, ctypes.c_int, _P, ctypes.c_int, _P, _I32, _I32, _I32,
+                                                   _F32, _U64, _U64, _P, _P, _P, _P, _P]
         lib.spec_verify_greedy.argtypes = [_P, ctypes.c_int, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]
         lib.spec_verify_tree.argtypes = [_P, ctypes.c_int, _P, ctypes.c_int, _P, _P, _I32, _I32, _I32, _F32,
                                          _U64, _U64, _P, _P, _P, _P, _SZ, _P]
@@ -60,7 +63,7 @@ def _lib():
                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]
         lib.spec_plug_tokens.argtypes = [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
         lib.spec_lookup_drafts.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
-        for fn in ("spec_verify_linear", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
+        for fn in ("spec_verify_linear", "spec_verify_linear_noalloc", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
                    "spec_lmhead_verify",
                    "spec_plug_tokens", "spec_lookup_drafts"):
             getattr(lib, fn).restype = ctypes.c_int
@@ -171,6 +174,24 @@ def spec_verify_linear(target_logits, draft_probs, draft_tokens, temperature, se
         _f32(out_target_prob, (B, k), "out_target_prob"), _f32(out_accept_prob, (B, k), "out_accept_prob"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_verify_linear")
+
+
+def spec_verify_linear_noalloc(target_logits, draft_probs, draft_tokens, temperature, seed, offset,
+                               out_tokens, out_accept_len, out_target_prob=None, out_accept_prob=None,
+                               stream=None):
+    """spec_verify_linear without a workspace (the library's static per-device scratch;
+    calls that overlap on one device race)."""
+    B, R, V = target_logits.shape
+    k = R - 1
+    if tuple(draft_probs.shape) != (B, k, V):
+        raise ValueError("draft_probs must have shape [B, k, V]")
+    rc = _lib().spec_verify_linear_noalloc(
+        _ptr(target_logits), _dt(target_logits), _ptr(draft_probs), _dt(draft_probs),
+        _i32(draft_tokens, (B, k), "draft_tokens"), B, k, V, float(temperature), int(seed), int(offset),
+        _i32(out_tokens, (B, R), "out_tokens"), _i32(out_accept_len, (B,), "out_accept_len"),
+        _f32(out_target_prob, (B, k), "out_target_prob"), _f32(out_accept_prob, (B, k), "out_accept_prob"),
+        _stream(stream))
+    _check(rc, "spec_verify_linear_noalloc")
 
 
 def spec_verify_greedy(target_logits, draft_tokens, out_tokens, out_accept_len, workspace=None, stream=None):

@@ -1,5 +1,6 @@
 // C-ABI entry points: validate on the host, carve the caller's workspace, enqueue the
 // kernels on the caller's stream.  Nothing here allocates or synchronises.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -25,6 +26,36 @@ int check_device() {
     }
     return state[dev] == 1 ? SV_OK : SV_E_DEVICE;
   }
+}
+
+// ---------------------------------------------------------------- static scratch
+// Backing store of spec_verify_linear_noalloc: the per-sequence and per-row words that
+// the other entry points keep in the caller's workspace.  One copy per device, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, never the device
+// array: its device address comes from hipGetSymbolAddress, resolved once per device
+// (with that device current) and cached below.
+constexpr size_t kScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's `scratch`, or nullptr if the runtime cannot give it.
+void* scratch_device_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+// Zero n 32-bit words (a fill kernel rather than a memset node, so that the call stays
+// safe to record in a graph).
+__global__ void zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 int head_max(const void* p, int32_t V, int dt) {
@@ -194,6 +225,32 @@ int spec_lmhead_verify(const void* hidden, const void* lm_head, const void* draf
                   workspace, st);
 }
 
+int spec_verify_linear_noalloc(const void* target_logits, int lt, const void* draft_probs, int qt,
+                               const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V, float temperature,
+                               uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_accept_len,
+                               float* out_target_prob, float* out_accept_prob, void* stream) {
+  sv::WsLayout L;
+  if (k >= 0 && sv::workspace_layout(SV_KIND_LINEAR, B, k, V, 0, &L) && L.total > kScratchBytes)
+    return SV_E_SCRATCH;
+  // the scratch stands in for the workspace in validation (any non-null pointer will do)
+  int rc = sv::validate_linear(target_logits, lt, draft_probs, qt, draft_tokens, B, k, V, temperature, out_tokens,
+                               out_accept_len, &kScratchBytes, kScratchBytes);
+  if (rc != SV_OK || B == 0) return rc;
+  if ((rc = check_device())) return rc;
+  void* ws = scratch_device_ptr();
+  if (ws == nullptr) return SV_E_DEVICE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  // the words must be zero on entry: clear the ones this call uses
+  const uint32_t words = static_cast<uint32_t>(L.total / 4);
+  const int blocks = static_cast<int>(std::min<uint32_t>(64u, (words + 255u) / 256u));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t*>(ws), words);
+  if (hipGetLastError() != hipSuccess) return SV_E_LAUNCH;
+  return run_rows(false, false, target_logits, lt, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature,
+                  seed, offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr,
+                  nullptr, ws, st);
+}
+
 size_t spec_verify_workspace_bytes(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H) {
   sv::WsLayout L;
   if (!sv::workspace_layout(kind, B, k_or_N, V, H, &L)) return 0;
@@ -212,6 +269,7 @@ const char* spec_verify_strerror(int code) {
     case SV_E_DEVICE: return "current HIP device is not gfx950";
     case SV_E_LAUNCH: return "kernel launch failed";
     case SV_E_ALIGN: return "tensor pointer is misaligned for its element type";
+    case SV_E_SCRATCH: return "sizes need more than the library's static scratch (1 MiB per device)";
     default: return "unknown error";
   }
 }

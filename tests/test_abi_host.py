@@ -241,3 +241,25 @@ def test_tree_binding_rejects_parent_count():
         sv.spec_verify_tree_lossless(lg, torch.zeros((1, 3), dtype=torch.int32), [-1, 0], 1.0, 0, 0,
                                      torch.zeros((1, 2), dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
 
+
+def linear_noalloc(**kw):
+    a = dict(logits=FAKE, lt=1, probs=FAKE, qt=1, tokens=FAKE, B=2, k=3, V=100, T=1.0, seed=0, off=0,
+             out=FAKE, alen=FAKE, tp=None, ap=None, stream=None)
+    a.update(kw)
+    return sv.library().spec_verify_linear_noalloc(*a.values())
+
+
+def test_linear_noalloc_validation_codes():
+    """The allocation-free call refuses sizes beyond its 1 MiB static scratch before any
+    device call, and otherwise validates like spec_verify_linear."""
+    ws = sv.spec_verify_workspace_bytes
+    assert ws(sv.SV_KIND_LINEAR, 40000, 5, 100) > (1 << 20)
+    assert linear_noalloc(B=40000, k=5) == -10
+    assert linear_noalloc(B=4096, k=63, V=8) == -10
+    assert linear_noalloc(B=0) == 0
+    assert linear_noalloc(logits=None) == -1
+    assert linear_noalloc(k=64) == -2
+    assert linear_noalloc(lt=4) == -3
+    assert linear_noalloc(T=0.0) == -4
+    assert linear_noalloc(logits=C(0x1001)) == -9
+    assert "scratch" in sv.spec_verify_strerror(-10)

@@ -1,0 +1,52 @@
+"""The allocation-free entry point (spec_verify_linear_noalloc) against spec_verify_linear
+on the same inputs: identical tokens, lengths and probabilities (both run the same
+kernels; only where the cross-workgroup words live differs).  Two calls in a row, the
+second smaller, so the second runs on what the first left in the static scratch; then a
+size beyond the scratch, refused on the host."""
+import numpy as np
+import pytest
+import torch
+
+import speculative_sampling_verify_03_amd as sv
+from gpu_common import announce, run_linear
+from synthetic import cfg2_case, linear_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_noalloc(case, T, seed, offset):
+    B, R, V = case.logits.shape
+    k = R - 1
+    out = dict(tokens=torch.full((B, R), -7, dtype=torch.int32, device=DEV),
+               accept_len=torch.full((B,), -7, dtype=torch.int32, device=DEV),
+               target_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV),
+               accept_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV))
+    sv.spec_verify_linear_noalloc(case.logits.to(DEV), case.draft_probs.to(DEV), case.draft_tokens.to(DEV), T, seed,
+                                  offset, out["tokens"], out["accept_len"], out["target_prob"], out["accept_prob"])
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in out.items()}
+
+
+@pytest.mark.parametrize("order", ["large_then_small", "small_then_large"])
+def test_noalloc_matches_workspace_call(order):
+    big = cfg2_case()                                            # B=64, k=5, V=32000 bf16
+    small = linear_case(8, 3, 1000, seed=21, dtype="f32", noise_sigma=1.0)
+    cases = [(big, 0, 0), (small, 5, 3)] if order == "large_then_small" else [(small, 5, 3), (big, 0, 0)]
+    for case, seed, offset in cases:
+        announce(f"noalloc: B={case.B} k={case.k} V={case.V} {case.logits.dtype}")
+        want = run_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset)
+        got = run_noalloc(case, case.temperature, seed, offset)
+        for key in ("tokens", "accept_len", "target_prob", "accept_prob"):
+            assert np.array_equal(got[key], want[key]), f"{key} differs for B={case.B}"
+        assert np.all(got["accept_len"] >= 0)
+
+
+def test_noalloc_refuses_sizes_beyond_scratch():
+    lg = torch.zeros((40000, 6, 8), dtype=torch.float32, device=DEV)
+    q = torch.zeros((40000, 5, 8), dtype=torch.float32, device=DEV)
+    x = torch.zeros((40000, 5), dtype=torch.int32, device=DEV)
+    toks = torch.zeros((40000, 6), dtype=torch.int32, device=DEV)
+    alen = torch.zeros((40000,), dtype=torch.int32, device=DEV)
+    with pytest.raises(sv.SpecVerifyError, match="SV_E_SCRATCH"):
+        sv.spec_verify_linear_noalloc(lg, q, x, 1.0, 0, 0, toks, alen)
