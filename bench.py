@@ -8,11 +8,15 @@ draft tokens and a 32000-token bfloat16 vocabulary; the metric is verified draft
 positions per second (B*k per step).  Other workloads (--workload) print their own line.
 
 Inputs are rotated over enough device copies (>= 1 GiB in total by default) that the
-256 MB Infinity Cache cannot serve a step from the previous step's reads.  Timing uses
-HIP events recorded on the stream the kernels run on, around exactly K steps, with a
+256 MB Infinity Cache cannot serve a step from the previous step's reads.  The K timed
+steps are recorded once into a HIP graph (one launch per step, rotating the inputs) and
+the graph is replayed, so the host's per-call cost (about 10 us of Python and ctypes per
+call) does not set the pace; if capture fails the steps are launched one by one.  Timing
+uses HIP events recorded on the stream the kernels run on, around exactly K steps, with a
 device synchronisation on both sides.  The JSON line carries a roofline block for the
-dominant kernel (algorithmic bytes per launch / average launch time, against 8 TB/s)
-and the CPU oracle timed on a bounded sample of the same workload on host cores.
+dominant kernel (algorithmic bytes per launch / average launch time, against 8 TB/s), the
+same bytes against a device copy measured in the same run, and the CPU oracle timed on a
+bounded sample of the same workload on host cores.
 """
 from __future__ import annotations
 
@@ -35,7 +39,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # a row whose digest no longer matches is stale and reported as null.
 _CSRC = "speculative_sampling_verify_03_amd/csrc/"
 KERNEL_SOURCES = {
-    "rows": [_CSRC + f for f in ("verify_rows.hip", "sv_device.hpp", "sv_launch.hpp", "api.hip")],
+    "rows": [_CSRC + f for f in ("verify_rows.hip", "verify_split.hip", "sv_device.hpp", "sv_launch.hpp", "api.hip",
+                                 "validate.hpp")],
     "greedy": [_CSRC + f for f in ("verify_greedy.hip", "sv_device.hpp", "sv_launch.hpp", "api.hip",
                                    "validate.cpp")],
     "lmhead": [_CSRC + f for f in ("lmhead_gemm.hip", "sv_device.hpp", "sv_launch.hpp")]
@@ -75,6 +80,7 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true", help="launch the timed steps one by one (no graph)")
     return ap.parse_args()
 
 
@@ -112,6 +118,10 @@ class Linear:
             self.launch_set(lg, q, x)
             torch.cuda.synchronize()
             self.rejected.append(int((self.alen < self.k).sum()))
+        # Only the split kernel writes the workspace's fixed prefix past its status word (its
+        # generation counters and tagged words); the row kernel leaves it at zero.
+        prefix = sv.spec_verify_workspace_bytes(self.ws_kind, 0, self.k, self.V)
+        self.split_path = int(self.ws[4:prefix].count_nonzero()) > 0
 
     def launch_set(self, lg, q, x):
         self.sv.spec_verify_linear(lg, q, x, self.T, 0, 0, self.tokens, self.alen, None, None, self.ws)
@@ -473,6 +483,72 @@ def copy_probe(torch, steps):
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}), flush=True)
 
 
+class Stepper:
+    """Runs K consecutive steps fn(0..K-1) on the current stream: as one replay of a graph
+    that recorded them (mode "hip_graph"), or launched one by one ("eager") when capture is
+    refused.  Each step's inputs are fixed when it is recorded, so a replay repeats exactly
+    the launches an eager loop would make."""
+
+    def __init__(self, torch, fn, K, use_graph=True):
+        self.torch, self.fn, self.K = torch, fn, K
+        self.graph = None
+        self.mode = "eager"
+        if use_graph:
+            try:
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    fn(0)  # first launches (per-device set-up) outside the capture
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(K):
+                        fn(i)
+                torch.cuda.synchronize()
+                self.graph = g
+                self.mode = "hip_graph"
+            except Exception as exc:  # capture refused: eager launches
+                self.mode = f"eager ({type(exc).__name__})"
+                torch.cuda.synchronize()
+
+    def run(self):
+        if self.graph is not None:
+            self.graph.replay()
+        else:
+            for i in range(self.K):
+                self.fn(i)
+
+    def time_ms(self, stream):
+        torch = self.torch
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        self.run()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+
+def copy_gbs(torch, stream, nbytes=1 << 30, reps=5):
+    """Device-to-device copy bandwidth (bytes read + written per second), the practical
+    streaming ceiling the verification kernels are compared with."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -493,40 +569,23 @@ def main():
     for i in range(args.warmup):
         wl.launch(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        wl.launch(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
+    stepper = Stepper(torch, wl.launch, args.steps, use_graph=not args.eager)
+    stepper.run()  # one untimed pass of the recorded steps
+    ms_total = stepper.time_ms(stream)
     ms_step = ms_total / args.steps
 
-    extra = {}
+    extra = {"launch": stepper.mode}
     if isinstance(wl, LinearPlug):
         # the plug's own cost: the step minus verification alone
-        torch.cuda.synchronize()
-        s2 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        s2.record(stream)
-        for i in range(args.steps):
-            wl.launch_verify_only(i)
-        e2.record(stream)
-        torch.cuda.synchronize()
-        extra["verify_ms"] = round(s2.elapsed_time(e2) / args.steps, 5)
+        vs = Stepper(torch, wl.launch_verify_only, args.steps, use_graph=not args.eager)
+        vs.run()
+        extra["verify_ms"] = round(vs.time_ms(stream) / args.steps, 5)
         extra["plug_ms"] = round(ms_step - extra["verify_ms"], 5)
     if isinstance(wl, LMHead):
         # the GEMM dominates: its time is the step minus the verification-only time
-        torch.cuda.synchronize()
-        s2 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        s2.record(stream)
-        for i in range(args.steps):
-            wl.launch_verify_only(i)
-        e2.record(stream)
-        torch.cuda.synchronize()
-        ms_verify = s2.elapsed_time(e2) / args.steps
+        vs = Stepper(torch, wl.launch_verify_only, args.steps, use_graph=not args.eager)
+        vs.run()
+        ms_verify = vs.time_ms(stream) / args.steps
         ms_gemm = ms_step - ms_verify
         achieved = wl.gemm_bytes() / (ms_gemm * 1e-3) / 1e9
         tflops = wl.gemm_flops() / (ms_gemm * 1e-3) / 1e12
@@ -541,6 +600,8 @@ def main():
         kname = {"Greedy": "greedy_flat_kernel", "Tree": "row_verify_kernel(tree)", "Lookup": "lookup_kernel",
                  "TreeLossless": "row_verify_kernel(tree, lossless)"}.get(type(wl).__name__,
                                                                                    "row_verify_kernel(linear)")
+        if type(wl).__name__ in ("Linear", "LinearPlug") and getattr(wl, "split_path", False):
+            kname = "row_split_kernel(linear)"
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
                     "kernel": kname, "kernel_ms": round(kernel_ms, 5),
@@ -556,7 +617,10 @@ def main():
         except ImportError:
             cpu_value, sample = wl.oracle_sample(args.cpu_seconds)
         cpu = {"value": round(cpu_value, 2), "unit": getattr(wl, "metric", "verified draft positions/sec").replace("/sec", "/s"), "cores": 1, "kind": "oracle",
-               "sample": sample}
+               "sample": sample, "host_cores_available": len(os.sched_getaffinity(0))}
+    copy_peak = copy_gbs(torch, stream)
+    roofline["copy_gbs"] = round(copy_peak, 1)
+    roofline["frac_of_copy"] = round(roofline["achieved"] / copy_peak, 4)
     line = {
         "metric": getattr(wl, "metric", "verified draft positions/sec"),
         "value": round(value, 1),

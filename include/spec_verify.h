@@ -35,11 +35,13 @@
  *     and returns; it never synchronises and never allocates.  Outputs are valid once that
  *     stream's work has completed.
  *   - `workspace` is caller-owned device memory of at least
- *     spec_verify_workspace_bytes(kind, ...) bytes.  Its first 4*B bytes are per-sequence
- *     arrival counters that MUST be zero when a call starts; every call returns them to
- *     zero before its last kernel ends, so a workspace zero-filled once (hipMemset,
- *     torch.zeros) stays valid for any later call on the same stream.  Calls that may run
- *     concurrently must not share a workspace.
+ *     spec_verify_workspace_bytes(kind, ...) bytes, zero-filled before its first use
+ *     (hipMemset, torch.zeros).  Every call leaves it valid for any later call on the same
+ *     stream (of any kind and sizes that fit it); its contents are the library's.  Calls
+ *     that may run concurrently must not share a workspace.  Its first 4 bytes are a
+ *     status word: non-zero after a call means a wait between the kernel's workgroups ran
+ *     out (only possible when other work holds the chip for a second or more) and that
+ *     call's outputs are not valid; it stays set until the caller clears it.
  *   - Return value: SV_OK (0) or a negative SV_E_* code, decided on the host before any
  *     launch (except SV_E_LAUNCH, reported when the runtime refuses a launch).
  *   - B = 0 is a valid empty call (nothing is launched).
@@ -105,13 +107,13 @@ SV_API int spec_verify_linear(const void* target_logits, int lt, const void* dra
  * spec_verify_linear without a workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments, kernels and results as spec_verify_linear, minus the workspace: the
- * per-sequence and per-row words live in a static device array of 1 MiB that the library
+ * per-sequence and per-row words live in a static device array of 4 MiB that the library
  * holds on every device it runs on until the process ends.  Each call clears the part it
  * uses (one small fill kernel on `stream`) and allocates nothing.  Every call on one
  * device shares that array, so calls that may overlap on one device (concurrent streams,
  * several host threads) race and must be serialised by the caller.
  * Returns SV_E_SCRATCH when spec_verify_workspace_bytes(SV_KIND_LINEAR, B, k, V, 0) exceeds
- * 1 MiB, decided before any device call.
+ * 4 MiB, decided before any device call.
  */
 SV_API int spec_verify_linear_noalloc(const void* target_logits, int lt, const void* draft_probs, int qt,
                        const int32_t* draft_tokens, int32_t B, int32_t k, int32_t V,

@@ -34,7 +34,7 @@ int check_device() {
 // the process ends.  In host code `scratch` names a host-side stand-in, never the device
 // array: its device address comes from hipGetSymbolAddress, resolved once per device
 // (with that device current) and cached below.
-constexpr size_t kScratchBytes = size_t(1) << 20;
+constexpr size_t kScratchBytes = size_t(4) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // Device address of this device's `scratch`, or nullptr if the runtime cannot give it.
@@ -117,6 +117,38 @@ int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* p
     }
   }
   (void)hipGetLastError();
+  // Linear batches whose rows, cut into slices of one tile each, all fit the chip at once
+  // take the split kernel: every row is reduced and drawn by several CUs together.
+  sv::SplitConfig sc;
+  if (!tree && sv::choose_split(bf16, qmode == 1 ? 1 : 0, V, head_max(logits, V, lt), static_cast<int64_t>(B) * R,
+                                &sc)) {
+    sv::SplitParams S{};
+    S.logits = logits;
+    S.probs = probs;
+    S.tokens = tokens;
+    S.B = B;
+    S.R = R;
+    S.V = V;
+    S.k = k;
+    S.S = sc.S;
+    S.chunk = sc.chunk;
+    S.q_bf16 = P.q_bf16;
+    S.c = P.c;
+    S.invT = 1.0 / P.T;
+    S.seed = seed;
+    S.offset = offset;
+    S.out_tokens = out_tokens;
+    S.out_accept_len = out_len;
+    S.out_tprob = tprob;
+    S.out_aprob = aprob;
+    char* w = static_cast<char*>(ws);
+    S.gen = reinterpret_cast<uint64_t*>(w + L.gen_off);
+    S.first_rej = reinterpret_cast<uint64_t*>(w + L.rej_off);
+    S.words = reinterpret_cast<uint64_t*>(w + L.words_off);
+    S.errword = reinterpret_cast<uint32_t*>(w + L.status_off);
+    const hipError_t e = sv::launch_split(S, bf16, qmode == 1 ? 1 : 0, sc, st);
+    return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
+  }
   const hipError_t e = sv::launch_rows(P, td, bf16, tree, qmode, rc.cfg, B * R, st);
   return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
 }
@@ -269,7 +301,7 @@ const char* spec_verify_strerror(int code) {
     case SV_E_DEVICE: return "current HIP device is not gfx950";
     case SV_E_LAUNCH: return "kernel launch failed";
     case SV_E_ALIGN: return "tensor pointer is misaligned for its element type";
-    case SV_E_SCRATCH: return "sizes need more than the library's static scratch (1 MiB per device)";
+    case SV_E_SCRATCH: return "sizes need more than the library's static scratch (4 MiB per device)";
     default: return "unknown error";
   }
 }

@@ -109,6 +109,16 @@ __device__ __forceinline__ Vec16 mask_edges(Vec16 v, int e0, int V) {
   return v;
 }
 
+// Opaque use of the packed row registers: the compiler must assume they changed, so
+// values unpacked from them earlier cannot be kept alive and reused later.  Holding the
+// unpacked floats would double the register footprint of a resident row.
+template <int NV>
+__device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    asm volatile("" : "+v"(buf[i].w[0]), "+v"(buf[i].w[1]), "+v"(buf[i].w[2]), "+v"(buf[i].w[3]));
+}
+
 // Scalar load of element i of a float32 (bf16 = false) or bfloat16 array.
 __device__ __forceinline__ float load_elem(const void* base, int64_t i, bool bf16) {
   if (bf16) return __uint_as_float(static_cast<uint32_t>(gptr<uint16_t>(base)[i]) << 16);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "validate.hpp"
+
 namespace sv {
 
 // Linear / tree row kernel.  R = k+1 rows per sequence (linear) or N nodes (tree).
@@ -52,6 +54,38 @@ RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows);
 // 2 float32 logits with 8-byte bfloat16 q chunks in phase with them.
 hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,
                        int grid, hipStream_t st);
+
+// Linear kernel with each row split over S co-resident workgroups (cooperative launch):
+// at most kSplitSlices slices per row, at most kSplitRows rows (the workspace holds slots
+// for those; validate.hpp).
+constexpr int kSplitShapeCount = 3;   // (threads, vectors per thread) instances
+struct SplitParams {
+  const void* logits;      // [B, R, V], float32 or bfloat16
+  const void* probs;       // [B, k, V]
+  const int32_t* tokens;   // [B, k]
+  int32_t B, R, V, k;
+  int32_t S, chunk;        // slices per row, vectors per slice
+  int32_t q_bf16;
+  float c;                 // log2(e) / T
+  double invT;             // 1 / T
+  uint64_t seed, offset;
+  int32_t* out_tokens;
+  int32_t* out_accept_len;
+  float* out_tprob;
+  float* out_aprob;
+  // The workspace's fixed prefix (validate.hpp): zero when the workspace is first used;
+  // afterwards each call leaves these words for the next (see verify_split.hip).
+  uint64_t* gen;           // [B] generation counters: generation = ticket >> 16
+  uint64_t* first_rej;     // [B] (generation << 8) | (64 - row) of the earliest rejection seen
+  uint64_t* words;         // [B * R][kSplitWordsPerRow] tagged words of each row
+  uint32_t* errword;       // sticky: set when a wait for another workgroup ran out
+};
+struct SplitConfig {
+  int shape, S, chunk, threads;
+};
+// qmode as for launch_rows (0 element loads, 1 vectors in phase); false = use the row kernel
+bool choose_split(bool bf16, int qmode, int V, int head_max, int64_t rows, SplitConfig* out);
+hipError_t launch_split(const SplitParams& P, bool bf16, int qmode, const SplitConfig& sc, hipStream_t st);
 
 // Greedy kernel: grid = B * R * S workgroups (S splits per row).
 struct GreedyParams {

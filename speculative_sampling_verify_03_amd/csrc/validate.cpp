@@ -51,11 +51,17 @@ bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H,
   }
   if (rows_per_seq > kMaxRows) return false;
   const size_t b = static_cast<size_t>(B);
-  out->counters_off = 0;
-  out->seq_off = round_up(b * sizeof(uint32_t));
-  out->row_off = out->seq_off + round_up(2 * b * sizeof(uint64_t));
-  out->total = out->row_off + round_up(b * static_cast<size_t>(rows_per_seq) * sizeof(uint64_t));
-  if (out->total == 0) out->total = kWsAlign;
+  const size_t rows = b * static_cast<size_t>(rows_per_seq);
+  const size_t w = sizeof(uint64_t);
+  const size_t splits = static_cast<size_t>(kSplitRows);
+  out->status_off = 0;
+  out->gen_off = kWsAlign;
+  out->rej_off = out->gen_off + round_up(splits * w);
+  out->words_off = out->rej_off + round_up(splits * w);
+  out->counters_off = out->words_off + round_up(splits * kSplitWordsPerRow * w);
+  out->seq_off = out->counters_off + round_up(b * sizeof(uint32_t));
+  out->row_off = out->seq_off + round_up(2 * b * w);
+  out->total = out->row_off + round_up(rows * w);
   return true;
 }
 

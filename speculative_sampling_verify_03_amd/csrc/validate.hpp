@@ -10,13 +10,28 @@ namespace sv {
 constexpr int kMaxRows = 64;   // k + 1 and N: one wave covers a sequence's rows
 constexpr size_t kWsAlign = 256;
 
-struct WsLayout {
-  size_t counters_off, seq_off, row_off, total;
-};
+// Every workspace, whatever the kind and sizes, starts with the same fixed prefix:
+//   status word u32 (first 256 bytes);
+//   generation counters u64[kSplitRows] and earliest-rejection words u64[kSplitRows], one
+//   per sequence of the split kernel;
+//   the split kernel's tagged words, kSplitWordsPerRow u64 per row for up to kSplitRows rows.
+// Its place never depends on the sizes, so words a split call leaves behind are never
+// read as anything else by a later call of any kind (they carry tags no later call will
+// look for).  After it come the sections of the row, greedy and tree kernels, which they
+// return to zero before they end: arrival counters u32[B], per-sequence words u64[B][2],
+// per-row words u64[B * rows] (rows = k + 1, or N for a tree).  Sections are 256-byte
+// aligned.
+constexpr int64_t kSplitRows = 2048;
+constexpr int kSplitSlices = 8;
+// per row: (max, sum) pair of each slice (4 words), the row's two uniforms (4 words),
+// residual mass of each slice (2 words), the row's decision (1 word)
+constexpr int kSplitWordsPerRow = 6 * kSplitSlices + 5;
 
-// Workspace layout for `kind` (SV_KIND_*): arrival counters u32[B], per-sequence words
-// u64[B][2], per-row words u64[B * rows] (rows = k + 1, or N for a tree); each section
-// 256-byte aligned.
+struct WsLayout {
+  size_t status_off, gen_off, rej_off, words_off;  // fixed prefix
+  size_t counters_off, seq_off, row_off;           // row kernel, greedy and tree kernels
+  size_t total;
+};
 bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H, WsLayout* out);
 // Number of workgroups each row is split over by the greedy kernel.
 int greedy_splits(int32_t B, int32_t R, int32_t V);

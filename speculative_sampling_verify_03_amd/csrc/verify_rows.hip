@@ -32,16 +32,6 @@
 
 namespace sv {
 
-// Opaque use of the packed row registers: the compiler must assume they changed, so
-// values unpacked from them earlier cannot be kept alive and reused later.  Holding the
-// unpacked floats would double the register footprint of a resident row.
-template <int NV>
-__device__ __forceinline__ void pin_packed(Vec16 (&buf)[NV]) {
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-    asm volatile("" : "+v"(buf[i].w[0]), "+v"(buf[i].w[1]), "+v"(buf[i].w[2]), "+v"(buf[i].w[3]));
-}
-
 // QMODE selects how the residual reads the draft-probability row q:
 //   kQVec  q has the logits' dtype and 16-byte phase: the same 16-byte vector loads;
 //   kQHalf float32 logits with bfloat16 q whose 8-byte chunks line up with the logits

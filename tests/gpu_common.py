@@ -29,6 +29,20 @@ def announce(msg: str) -> None:
     print(f"[gpu-test] {msg}", flush=True)
 
 
+def status_word(ws: torch.Tensor) -> int:
+    """The workspace's status word (its first 4 bytes): non-zero when a wait between a
+    kernel's workgroups ran out."""
+    return int(ws[:4].clone().view(torch.int32).item())
+
+
+def sections_clear(ws: torch.Tensor, kind: int, k_or_N: int, V: int) -> bool:
+    """Everything after the workspace's fixed prefix is zero: the row, greedy and tree
+    kernels return their words to zero before they end (the prefix, whose size is the
+    workspace size of an empty batch, holds the split kernel's tagged words, which stay)."""
+    prefix = sv.spec_verify_workspace_bytes(kind, 0, k_or_N, V)
+    return int(ws[prefix:].count_nonzero()) == 0
+
+
 def on_device(t: torch.Tensor, misalign: int = 0) -> torch.Tensor:
     """Copy to the GPU; with misalign = m the data starts m elements past an aligned
     allocation (so the base pointer is not 16-byte aligned)."""

@@ -221,6 +221,16 @@ void workspace() {
           ++failures;
         }
       }
+  // the prefix never moves with the sizes or the kind
+  sv::WsLayout A, Bl;
+  EXPECT(sv::workspace_layout(SV_KIND_LINEAR, 64, 5, 32000, 0, &A), true);
+  EXPECT(sv::workspace_layout(SV_KIND_TREE, 3, 61, 7, 0, &Bl), true);
+  ++checks;
+  if (A.status_off != Bl.status_off || A.gen_off != Bl.gen_off || A.rej_off != Bl.rej_off ||
+      A.words_off != Bl.words_off || A.counters_off != Bl.counters_off || A.counters_off <= A.words_off) {
+    std::printf("FAIL the workspace prefix moved between layouts\n");
+    ++failures;
+  }
   EXPECT(sv::workspace_layout(7, 1, 1, 1, 1, &L), false);
   EXPECT(sv::workspace_layout(SV_KIND_LINEAR, -1, 1, 1, 1, &L), false);
   EXPECT(sv::workspace_layout(SV_KIND_LINEAR, 1, 1, 0, 1, &L), false);

@@ -250,12 +250,13 @@ def linear_noalloc(**kw):
 
 
 def test_linear_noalloc_validation_codes():
-    """The allocation-free call refuses sizes beyond its 1 MiB static scratch before any
+    """The allocation-free call refuses sizes beyond its 4 MiB static scratch before any
     device call, and otherwise validates like spec_verify_linear."""
     ws = sv.spec_verify_workspace_bytes
-    assert ws(sv.SV_KIND_LINEAR, 40000, 5, 100) > (1 << 20)
-    assert linear_noalloc(B=40000, k=5) == -10
-    assert linear_noalloc(B=4096, k=63, V=8) == -10
+    assert ws(sv.SV_KIND_LINEAR, 100000, 5, 100) > (4 << 20)
+    assert ws(sv.SV_KIND_LINEAR, 30000, 5, 100) < (4 << 20)
+    assert linear_noalloc(B=100000, k=5) == -10
+    assert linear_noalloc(B=8192, k=63, V=8) == -10
     assert linear_noalloc(B=0) == 0
     assert linear_noalloc(logits=None) == -1
     assert linear_noalloc(k=64) == -2

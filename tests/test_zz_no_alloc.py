@@ -43,10 +43,11 @@ def test_noalloc_matches_workspace_call(order):
 
 
 def test_noalloc_refuses_sizes_beyond_scratch():
-    lg = torch.zeros((40000, 6, 8), dtype=torch.float32, device=DEV)
-    q = torch.zeros((40000, 5, 8), dtype=torch.float32, device=DEV)
-    x = torch.zeros((40000, 5), dtype=torch.int32, device=DEV)
-    toks = torch.zeros((40000, 6), dtype=torch.int32, device=DEV)
-    alen = torch.zeros((40000,), dtype=torch.int32, device=DEV)
+    B = 100000
+    lg = torch.zeros((B, 6, 8), dtype=torch.float32, device=DEV)
+    q = torch.zeros((B, 5, 8), dtype=torch.float32, device=DEV)
+    x = torch.zeros((B, 5), dtype=torch.int32, device=DEV)
+    toks = torch.zeros((B, 6), dtype=torch.int32, device=DEV)
+    alen = torch.zeros((B,), dtype=torch.int32, device=DEV)
     with pytest.raises(sv.SpecVerifyError, match="SV_E_SCRATCH"):
         sv.spec_verify_linear_noalloc(lg, q, x, 1.0, 0, 0, toks, alen)
