@@ -58,7 +58,7 @@ hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool t
 // Linear kernel with each row split over S co-resident workgroups (cooperative launch):
 // at most kSplitSlices slices per row, at most kSplitRows rows (the workspace holds slots
 // for those; validate.hpp).
-constexpr int kSplitShapeCount = 3;   // (threads, vectors per thread) instances
+constexpr int kSplitShapeCount = 4;   // (threads, vectors per thread) instances
 struct SplitParams {
   const void* logits;      // [B, R, V], float32 or bfloat16
   const void* probs;       // [B, k, V]

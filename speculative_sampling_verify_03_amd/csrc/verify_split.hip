@@ -556,7 +556,10 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
 struct SplitShape {
   int nt, nv;
 };
-static const SplitShape kSplitShapes[kSplitShapeCount] = {{256, 4}, {256, 8}, {128, 8}};
+// Tried in this order; for one vocabulary size fewer, wider slices run faster (B=64 k=5
+// V=32000 bf16: 2 slices of 512 x 4 14.4 us, 3 of 384 x 4 15.8, 4 of 256 x 4 15.9,
+// 2 of 1024 x 2 15.9, 2 of 256 x 8 15.0).
+static const SplitShape kSplitShapes[kSplitShapeCount] = {{512, 4}, {256, 4}, {256, 8}, {128, 8}};
 
 template <bool BF16, int NT, int NV, int QMODE>
 static const void* split_fn() {
@@ -566,8 +569,9 @@ static const void* split_fn() {
 template <bool BF16, int QMODE>
 static const void* split_fn_shape(int shape) {
   switch (shape) {
-    case 0: return split_fn<BF16, 256, 4, QMODE>();
-    case 1: return split_fn<BF16, 256, 8, QMODE>();
+    case 0: return split_fn<BF16, 512, 4, QMODE>();
+    case 1: return split_fn<BF16, 256, 4, QMODE>();
+    case 2: return split_fn<BF16, 256, 8, QMODE>();
     default: return split_fn<BF16, 128, 8, QMODE>();
   }
 }

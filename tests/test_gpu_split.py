@@ -1,6 +1,7 @@
 """GPU parity of linear verification on batches that take the split path: every row cut
 into S slices (2 <= S <= 8), one workgroup each, all resident together.  The B=64, k=5,
-V=32000 workload is cut into 4 slices per row; the cases below cover 2 to 8 slices, every
+V=32000 workload is cut into 2 slices of 512 x 4 per row; the cases below cover 2 to 8
+slices and the narrower shapes taken when the wider ones do not fit the chip, every
 way a row can end (accepted, rejected with a residual draw, the bonus draw), rows that
 reject everywhere or nowhere, k = 0, unaligned bases and draft rows read element-wise,
 repeated calls on one workspace (the tagged words of one call must never be taken for
@@ -37,13 +38,15 @@ def test_headline_batches(case_seed):
 
 
 @pytest.mark.parametrize("dtype,V,B,k", [
-    ("bf16", 8193, 64, 3),     # 2 slices
-    ("bf16", 20001, 64, 4),    # 3 slices, ragged end
-    ("bf16", 65536, 32, 5),    # 8 slices of 256 x 4
-    ("bf16", 100000, 16, 5),   # 7 slices of 256 x 8
-    ("f32", 5000, 48, 4),      # 2 slices
-    ("f32", 16000, 40, 5),     # 4 slices
-    ("f32", 40000, 24, 5),     # 5 slices of 256 x 8
+    ("bf16", 8193, 64, 3),     # 2 slices of 256 x 4
+    ("bf16", 20001, 64, 4),    # 2 slices of 512 x 4, ragged end
+    ("bf16", 65536, 32, 5),    # 192 rows: 5 slices of 256 x 8 (5 x 512 x 4 do not fit)
+    ("bf16", 100000, 16, 5),   # 7 slices of 512 x 4
+    ("bf16", 32000, 80, 5),    # 480 rows: 512 x 4 and 256 x 4 do not fit, 2 slices of 256 x 8
+    ("bf16", 12000, 160, 5),   # 960 rows: 2 slices of 128 x 8 (wider shapes do not fit)
+    ("f32", 5000, 48, 4),      # 2 slices of 256 x 4
+    ("f32", 16000, 40, 5),     # 2 slices of 512 x 4
+    ("f32", 40000, 24, 5),     # 5 slices of 512 x 4
 ])
 def test_slice_counts(dtype, V, B, k):
     case = linear_case(B, k, V, seed=V + B, dtype=dtype, noise_sigma=1.0)
