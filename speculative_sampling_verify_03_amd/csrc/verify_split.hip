@@ -104,6 +104,43 @@ __device__ __forceinline__ uint32_t join32(uint32_t half) {
   return half | (static_cast<uint32_t>(__shfl_down(static_cast<int>(half), 1)) << 16);
 }
 
+// One inverse-CDF step over weights held one per lane (w >= 0; lanes past the count hold
+// 0), with its target t: the first lane of positive weight whose inclusive prefix exceeds t,
+// with that lane's exclusive prefix in `before`.  When none does (t at or past the total,
+// through rounding) or `clamp` is already set, the last lane of positive weight, and
+// `clamp` is set (every level below then takes its last positive weight too).  -1 when
+// every weight is 0.  The prefixes come from a tree-ordered scan, so they need not grow
+// from lane to lane by exactly each lane's weight: a lane of zero weight is never taken.
+__device__ __forceinline__ int pick_lane(float w, float incl, float t, bool& clamp, float& before) {
+  const uint64_t pos = __ballot(w > 0.f);
+  const uint64_t hit = clamp ? 0ull : __ballot(w > 0.f && incl > t);
+  before = 0.f;
+  if (hit) {
+    const int l = __ffsll(static_cast<long long>(hit)) - 1;
+    if (l > 0) before = lane_value(incl, l - 1);
+    return l;
+  }
+  clamp = true;
+  return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
+}
+
+// Inclusive prefix sums over lanes 0..7 (valid in those lanes; the slices of a row and the
+// waves of a workgroup are at most 8).
+__device__ __forceinline__ float scan8(float x) {
+  x += dpp_f<kDppShr1>(0.f, x);
+  x += dpp_f<kDppShr2>(0.f, x);
+  x += dpp_f<kDppShr4>(0.f, x);
+  return x;
+}
+// The (max, sum) pairs of lanes 0..7 merged (the same order wherever it runs), in every lane.
+__device__ __forceinline__ void merge_pairs8(float& m, float& s, float c) {
+  merge_step<kDppShr1>(m, s, c);
+  merge_step<kDppShr2>(m, s, c);
+  merge_step<kDppShr4>(m, s, c);
+  m = lane_value(m, 7);
+  s = lane_value(s, 7);
+}
+
 template <bool BF16>
 __device__ __forceinline__ Vec16 ninf_vec() {
   Vec16 v;
@@ -113,6 +150,9 @@ __device__ __forceinline__ Vec16 ninf_vec() {
 }
 
 constexpr uint32_t kKept = 1u, kRejected = 2u;  // decision word payloads
+// Draws from p leave out vectors whose weight sum (against a largest weight of 1) is below
+// 2^-122: such a vector's largest element, one of at most 8, is then at least 2^-125.
+constexpr float kTinyMass = 0x1p-122f;
 constexpr uint32_t kMassSkip = 0x80000000u;     // in a residual mass (a sign bit): the row stands down
 // a row's words: 4 per slice for its (max, sum) pair and 4 right after the S pairs for the
 // row's uniforms (written by slice 0), 2 per slice for its residual mass, 1 for the row's
@@ -128,10 +168,12 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   constexpr int VE = E::kPerVec;
   constexpr int EB = E::kBytes;
   constexpr int NW = NT / kWave;
-  __shared__ float s_wm[NW], s_ws[NW], s_wt[NW];                                // per wave: pass-1 pair, draw total
-  __shared__ float s_pm[kSplitSlices], s_ps[kSplitSlices], s_pt[kSplitSlices];  // per slice of the row
-  __shared__ float s_uacc, s_usmp;
-  __shared__ int s_cand, s_skip;
+  __shared__ float s_wm[NW], s_ws[NW], s_wt[NW];  // per wave: pass-1 pair, draw total
+  __shared__ float s_m, s_Z;                      // the row's (max, sum)
+  // the slice that draws: its index, the target t = u * S and the mass of the slices
+  // before it; clamp: t lay past the total
+  __shared__ float s_t, s_before;
+  __shared__ int s_cand, s_skip, s_win, s_clamp, s_fromp;
   __shared__ uint64_t s_gen;
 
   const int tid = threadIdx.x;
@@ -252,41 +294,58 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       (void)__hip_atomic_fetch_add(&P.gen[b], (1ull << 16) - static_cast<uint64_t>(RS), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
   }
+  // Wave 0 polls, merges the pairs (a lane-parallel merge: the same order in every slice,
+  // so all of them hold bit-identical (m, Z)), takes the acceptance decision (lane 0 =
+  // thread 0, which holds the draft token's gathered values) and, for a draw from p, picks
+  // the slice from the pairs rescaled to the row maximum.  Its picks stay in its registers
+  // for a residual that turns out empty.
+  double g_e = 0.0;
+  float u_smp_w = 0.f, fp_t = 0.f, fp_before = 0.f;
+  int fp_win = -1;
+  bool fp_clamp = false;
   if (wid == 0) {
     // lane 4s + 0..3: halves of slice s's max, then of its sum; lanes 4S + 0..3: halves of
     // the two uniforms
     const uint32_t v = join32(wait_tagged(row_words + kPairWord, 1, 4 * S + 4, tag, lane, P.errword));
-    const uint32_t vz = __shfl_down(static_cast<int>(v), 2);
-    if (lane <= 4 * S && (lane & 3) == 0) {
-      if (lane < 4 * S) {
-        s_pm[lane / 4] = __uint_as_float(v);
-        s_ps[lane / 4] = __uint_as_float(vz);
-      } else {
-        s_uacc = __uint_as_float(v);
-        s_usmp = __uint_as_float(vz);
-      }
-    }
-  }
-  __syncthreads();
-  u_acc = s_uacc;
-  u_smp = s_usmp;
-  float m = -INFINITY, Z = 0.f;
-  for (int t = 0; t < S; ++t) merge_max_sum(m, Z, s_pm[t], s_ps[t], c);  // same order in every slice
-
-  // ---- acceptance test (thread 0; every slice reaches the same result, slice 0 reports it):
-  // u * q(x) < p(x) = e / Z with e = exp((l_x - m) / T) in float64, compared as
-  // u * q(x) * Z < e so that no division sits on the path to the decision
-  double g_e = 0.0;
-  if (tid == 0) {
+    const uint32_t vz = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), 2));
+    const float u_acc_w = __uint_as_float(static_cast<uint32_t>(lane_value(static_cast<int>(v), 4 * S)));
+    u_smp_w = __uint_as_float(static_cast<uint32_t>(lane_value(static_cast<int>(vz), 4 * S)));
+    // slice s's pair to lane s (every lane takes part in the shuffles)
+    const uint32_t gm = static_cast<uint32_t>(__shfl(static_cast<int>(v), (4 * lane) & (kWave - 1)));
+    const uint32_t gz = static_cast<uint32_t>(__shfl(static_cast<int>(vz), (4 * lane) & (kWave - 1)));
+    const float pm = lane < S ? __uint_as_float(gm) : -INFINITY;
+    const float ps = lane < S ? __uint_as_float(gz) : 0.f;
+    float mr = pm, zr = ps;
+    merge_pairs8(mr, zr, c);
+    // acceptance test: u * q(x) < p(x) = e / Z with e = exp((l_x - m) / T) in float64,
+    // compared as u * q(x) * Z < e so that no division sits on the path to the decision
     bool acc = false;
-    if (j < k) {
-      if (g_valid) g_e = exp((static_cast<double>(g_l) - static_cast<double>(m)) * P.invT);
-      acc = g_valid && (static_cast<double>(u_acc) * static_cast<double>(g_q) * static_cast<double>(Z) < g_e);
+    if (lane == 0 && j < k) {
+      if (g_valid) g_e = exp((static_cast<double>(g_l) - static_cast<double>(mr)) * P.invT);
+      acc = g_valid && (static_cast<double>(u_acc_w) * static_cast<double>(g_q) * static_cast<double>(zr) < g_e);
     }
-    s_cand = (j == k) || !acc;
-    s_skip = 0;
+    // a draw from p: slice masses against the row maximum.  A slice whose mass is below
+    // twice kTinyMass per vector it holds is left out, so that a slice taken holds a
+    // vector that is not left out below.
+    float ms = lane < S ? ps * fast_exp2((pm - mr) * c) : 0.f;
+    if (ms < 2.f * kTinyMass * static_cast<float>(NT * NV)) ms = 0.f;
+    const float incl = scan8(ms);
+    fp_t = u_smp_w * lane_value(incl, 7);
+    fp_win = pick_lane(ms, incl, fp_t, fp_clamp, fp_before);
+    if (lane == 0) {
+      s_m = mr;
+      s_Z = zr;
+      s_cand = (j == k) || !acc;
+      s_skip = 0;
+      s_fromp = 1;
+      s_win = fp_win;
+      s_t = fp_t;
+      s_before = fp_before;
+      s_clamp = fp_clamp;
+    }
   }
   __syncthreads();
+  const float m = s_m, Z = s_Z;
   const bool cand = s_cand != 0;
   const bool resid_row = cand && j < k;
 
@@ -348,21 +407,15 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) w[e] = fast_exp2((E::at(lv, e) - m) * c);
   };
-  // slot totals (wave scans) of seg[] and the wave total as their sequential sum
-  auto slot_totals = [&]() -> float {
-    float wt = 0.f;
+  // the wave's total of seg[] (one reduction; the walking wave later sums each slot on its
+  // own, which may differ from it in the last bits: the walk's clamping covers that)
+  auto wave_total = [&]() -> float {
+    float ts = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      slot_tot[i] = lane_value(wave_inclusive_scan(seg[i]), 63);
-      wt += slot_tot[i];
-    }
-    return wt;
+    for (int i = 0; i < NV; ++i) ts += seg[i];
+    return wave_sum(ts);
   };
 
-  bool from_p = !resid_row;
-  int winner = -1;
-  float t = 0.f, before = 0.f;
-  bool clamp = false;  // a target past a level's total: every level below takes its last positive weight
   if (resid_row) {
     // ---- residual at a rejected position.  A row that is not the sequence's first
     // rejection stands down once any of its slices has seen an earlier one; the slices
@@ -376,7 +429,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       for (int e = 0; e < VE; ++e) sg += w[e];
       seg[i] = sg;
     }
-    const float wt = slot_totals();
+    const float wt = wave_total();
     if (lane == 0) s_wt[wid] = wt;
     __syncthreads();
     if (publisher) {
@@ -386,71 +439,50 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       put32(row_words + kMassWord + 2 * slice, tag, __float_as_uint(mass) | (skip_mine ? kMassSkip : 0u));
     }
     if (wid == 0) {
-      // lane 2s + 0..1: halves of slice s's residual mass
+      // lane 2s + 0..1: halves of slice s's residual mass; slice s's mass to lane s
       const uint32_t v = join32(wait_tagged(row_words + kMassWord, 1, 2 * S, tag, lane, P.errword));
       const bool any_skip = __ballot(lane < 2 * S && (lane & 1) == 0 && (v & kMassSkip)) != 0;
-      if (lane < 2 * S && (lane & 1) == 0) s_pt[lane / 2] = __uint_as_float(v & ~kMassSkip);
-      if (lane == 0) s_skip = any_skip;
+      const uint32_t g = static_cast<uint32_t>(__shfl(static_cast<int>(v), (2 * lane) & (kWave - 1)));
+      const float mass = lane < S ? __uint_as_float(g & ~kMassSkip) : 0.f;
+      const float incl = scan8(mass);
+      const float tot = lane_value(incl, 7);
+      bool cl = false;
+      float bef = 0.f;
+      const float tt = u_smp_w * tot;
+      const int win = tot > 0.f ? pick_lane(mass, incl, tt, cl, bef) : -1;
+      if (lane == 0) {
+        s_skip = any_skip;
+        if (win >= 0) {  // else the residual is empty through rounding: the draw from p stands
+          s_fromp = 0;
+          s_win = win;
+          s_t = tt;
+          s_before = bef;
+          s_clamp = cl;
+        }
+      }
     }
     __syncthreads();
     if (s_skip) return;  // uniform: an earlier row rejected, this row's token is not needed
-    float tot = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) tot += s_pt[s2];
-    if (tot > 0.f) {
-      t = u_smp * tot;
-      float cum = 0.f;
-      int last_pos = -1;
-      for (int s2 = 0; s2 < S; ++s2) {
-        const float nc = cum + s_pt[s2];
-        if (s_pt[s2] > 0.f) last_pos = s2;
-        if (winner < 0 && nc > t) {
-          winner = s2;
-          before = cum;
-        }
-        cum = nc;
-      }
-      if (winner < 0) {  // t past the total (not reachable: the walk repeats the total's sum)
-        winner = last_pos;
-        clamp = true;
-      }
-    } else {
-      from_p = true;  // residual empty through rounding: draw from p itself
-    }
   }
+  const bool from_p = s_fromp != 0;
+  const int winner = s_win;
+  const float t = s_t, before = s_before;
+  bool clamp = s_clamp != 0;
+  if (winner != slice) return;  // uniform
   if (from_p) {
-    // ---- draw from p: slice masses from the pass-1 pairs, rescaled to the row maximum
-    float tot = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) tot += s_ps[s2] * fast_exp2((s_pm[s2] - m) * c);
-    t = u_smp * tot;
-    float cum = 0.f;
-    int last_pos = -1;
-    winner = -1;
-    clamp = false;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float ms = s_ps[s2] * fast_exp2((s_pm[s2] - m) * c);
-      const float nc = cum + ms;
-      if (ms > 0.f) last_pos = s2;
-      if (winner < 0 && nc > t) {
-        winner = s2;
-        before = cum;
-      }
-      cum = nc;
-    }
-    if (winner < 0) {
-      winner = last_pos;
-      clamp = true;
-    }
-    if (winner != slice) return;  // uniform
-    // this slice's vector sums of p against the row maximum: pass 1's sums, rescaled
-    // from each thread's own reference
+    // this slice's vector sums of p against the row maximum: pass 1's sums, rescaled from
+    // each thread's own reference; a vector whose sum is below kTinyMass is left out, so
+    // that a vector taken holds an element whose own weight is a normal number
     const float scale = own_any ? fast_exp2((ref - m) * c) : 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) seg[i] = seg_p[i] * scale;
-    const float wt = slot_totals();
+    for (int i = 0; i < NV; ++i) {
+      const float v = seg_p[i] * scale;
+      seg[i] = v >= kTinyMass ? v : 0.f;
+    }
+    const float wt = wave_total();
     if (lane == 0) s_wt[wid] = wt;
     __syncthreads();
   }
-  if (winner != slice) return;  // uniform
 
   // ---- walk: wave, then slot, then lane, then element (each level sums the values the
   // level above summed, up to the rescaling of a draw from p; a target past a level's
@@ -459,23 +491,17 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   // the draw only when u lies within about 1e-7 of a boundary, far inside the near-tie
   // band of 1e-6 that parity with the float64 oracle leaves out.
   const float t1 = t - before;
-  int wstar = -1, wlast = -1;
-  float wcum = 0.f, wbefore = 0.f;
-  for (int w = 0; w < NW; ++w) {
-    const float nc = wcum + s_wt[w];
-    if (s_wt[w] > 0.f) wlast = w;
-    if (!clamp && wstar < 0 && nc > t1) {
-      wstar = w;
-      wbefore = wcum;
-    }
-    wcum = nc;
+  float wbefore = 0.f;
+  int wstar;
+  {
+    const float wv = lane < NW ? s_wt[lane < NW ? lane : 0] : 0.f;
+    wstar = pick_lane(wv, scan8(wv), t1, clamp, wbefore);
   }
-  if (wstar < 0) {
-    wstar = wlast < 0 ? 0 : wlast;
-    clamp = true;
-  }
+  if (wstar < 0) wstar = 0;  // no positive weight (not reachable for finite inputs)
   if (wid != wstar) return;
   const float t2 = t1 - wbefore;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) slot_tot[i] = wave_sum(seg[i]);
   int istar = -1, ilast = -1;
   float icum = 0.f, ibefore = 0.f;
 #pragma unroll
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     }
   const float scan = wave_inclusive_scan(sg);
   const float t3 = t2 - ibefore;
-  const uint64_t hit = __ballot(scan > t3);
+  const uint64_t hit = __ballot(sg > 0.f && scan > t3);  // a tree-ordered scan: see pick_lane
   const uint64_t pos = __ballot(sg > 0.f);
   int lstar;
   if (!clamp && hit) {
@@ -533,7 +559,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
         if (!clamp && ye < 0 && ec > t4) ye = e;
       }
     }
-    if (ye < 0) ye = ylast;
+    if (ye < 0) ye = ylast < 0 ? 0 : ylast;  // (no positive weight: not reachable for finite inputs)
     y = vi * VE - h + ye;
   }
   y = lane_value(y, lstar);
