@@ -585,7 +585,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           if (i == istar) sg = seg[i];
         const float scan = wave_inclusive_scan(sg);
         const double t2 = t1 - static_cast<double>(ibefore);
-        const uint64_t hit = __ballot(static_cast<double>(scan) > t2);
+        // (the scan is tree-ordered: its prefixes need not grow by exactly each lane's
+        // weight, so a lane of zero weight is never taken)
+        const uint64_t hit = __ballot(sg > 0.f && static_cast<double>(scan) > t2);
         const uint64_t pos = __ballot(sg > 0.f);
         int lstar;
         if (!clamp && hit) {

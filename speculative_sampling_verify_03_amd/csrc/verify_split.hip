@@ -124,6 +124,18 @@ __device__ __forceinline__ int pick_lane(float w, float incl, float t, bool& cla
   return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
 }
 
+// A 16-byte load of vector i, or of vector 0 when i is out of range, with nothing applied
+// to the result: a consumer in the same branch would make the wave wait for the load there.
+__device__ __forceinline__ Vec16 ld16_raw(const SV_GLOBAL Vec16* p, int i, int n) {
+  const SV_GLOBAL Vec16& g = p[static_cast<unsigned>(i) < static_cast<unsigned>(n) ? i : 0];
+  Vec16 v;
+  v.w[0] = g.w[0];
+  v.w[1] = g.w[1];
+  v.w[2] = g.w[2];
+  v.w[3] = g.w[3];
+  return v;
+}
+
 // Inclusive prefix sums over lanes 0..7 (valid in those lanes; the slices of a row and the
 // waves of a workgroup are at most 8).
 __device__ __forceinline__ float scan8(float x) {
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   // the slice that draws: its index, the target t = u * S and the mass of the slices
   // before it; clamp: t lay past the total
   __shared__ float s_t, s_before;
-  __shared__ int s_cand, s_skip, s_win, s_clamp, s_fromp;
+  __shared__ int s_cand, s_skip, s_skipmine, s_win, s_clamp, s_fromp;
   __shared__ uint64_t s_gen;
 
   const int tid = threadIdx.x;
@@ -350,29 +362,33 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   const bool resid_row = cand && j < k;
 
   // Memory reads first, then the stores: a wave's wait for a read also waits for whatever
-  // it issued before it.
+  // it issued before it.  The draft vectors are used as loaded: where a vector lies past
+  // this slice's share, or an element outside the row, the logit is -inf and the residual
+  // weight max(0, 0 - q) is 0 whatever q holds (a probability of this row or the next).
   Vec16 qv[(QMODE == kQVecS) ? NV : 1];
   if (resid_row && QMODE == kQVecS) {
     const uintptr_t qa = reinterpret_cast<uintptr_t>(qrowp);
     const SV_GLOBAL Vec16* vq = gptr<Vec16>(reinterpret_cast<const void*>(qa - (qa & 15)));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) qv[i] = ld16(vq, v0 + i * kWave, vend);
+    for (int i = 0; i < NV; ++i) qv[i] = ld16_raw(vq, v0 + i * kWave, vend);
   }
   // the decisions of the sequence's earlier rows (lane l: row l), read by every wave now so
   // that whichever wave draws the token finds them in its registers
   uint64_t dec_early = 0;
-  if (cand && lane < j) dec_early = word_get(seq_words + kDecisionWord + static_cast<size_t>(lane) * kSplitWordsPerRow);
-  // The publisher reports the decision (slice 0) and, for a rejection, the earliest
-  // rejection seen so far, so that later rejected rows can stand down (generation in the
-  // high bits: a word from an earlier call never outranks this one); each slice of a
-  // rejected row reads that word back, to decide whether to stand down.
+  int tok_early = -1;  // and the sequence's draft tokens, which the outputs repeat
+  if (cand && lane < j) {
+    dec_early = word_get(seq_words + kDecisionWord + static_cast<size_t>(lane) * kSplitWordsPerRow);
+    tok_early = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * k + lane];
+  }
+  // The publisher of slice 0 reports the decision and, for a rejection, raises the
+  // sequence's earliest-rejection word (generation in the high bits: a word from an earlier
+  // call never outranks this one); thread 0 of each slice of a rejected row reads that word,
+  // so that a row that is not the sequence's first rejection can stand down.
   uint64_t rej_seen = 0;
-  if (publisher && j < k) {
-    if (slice == 0) {
-      word_put(row_words + kDecisionWord, tagged(tag, cand ? kRejected : kKept));
-      if (cand) (void)atomic_max_u64(&P.first_rej[b], (gen << 8) | static_cast<uint64_t>(64 - j));
-    }
-    if (cand) rej_seen = __hip_atomic_load(&P.first_rej[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && resid_row) rej_seen = __hip_atomic_load(&P.first_rej[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (publisher && slice == 0 && j < k) {
+    word_put(row_words + kDecisionWord, tagged(tag, cand ? kRejected : kKept));
+    if (cand) (void)atomic_max_u64(&P.first_rej[b], (gen << 8) | static_cast<uint64_t>(64 - j));
   }
   // p(x) and min(1, p/q) for the caller (slice 0 of a draft row), once the reads are issued
   if (tid == 0 && slice == 0 && j < k) {
@@ -407,8 +423,9 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) w[e] = fast_exp2((E::at(lv, e) - m) * c);
   };
-  // the wave's total of seg[] (one reduction; the walking wave later sums each slot on its
-  // own, which may differ from it in the last bits: the walk's clamping covers that)
+  // the wave's total of seg[] in one reduction, so that the mass goes out first; the slot
+  // totals follow while it travels and may differ from their sum in the last bits, which
+  // the walk's clamping covers
   auto wave_total = [&]() -> float {
     float ts = 0.f;
 #pragma unroll
@@ -418,8 +435,9 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
 
   if (resid_row) {
     // ---- residual at a rejected position.  A row that is not the sequence's first
-    // rejection stands down once any of its slices has seen an earlier one; the slices
-    // compute their masses meanwhile rather than wait for that word.
+    // rejection stands down once any of its slices has seen an earlier one: that slice
+    // flags its mass word and ends, the others end on reading the flag.  The slices
+    // compute their masses meanwhile rather than wait for the word they read.
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float w[VE];
@@ -431,13 +449,18 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     }
     const float wt = wave_total();
     if (lane == 0) s_wt[wid] = wt;
+    if (tid == 0) s_skipmine = (rej_seen >> 8) == gen && static_cast<int>(rej_seen & 0xff) > 64 - j;
     __syncthreads();
+    const bool skip_mine = s_skipmine != 0;
     if (publisher) {
-      const bool skip_mine = (rej_seen >> 8) == gen && static_cast<int>(rej_seen & 0xff) > 64 - j;
       float mass = 0.f;
       for (int w = 0; w < NW; ++w) mass += s_wt[w];
       put32(row_words + kMassWord + 2 * slice, tag, __float_as_uint(mass) | (skip_mine ? kMassSkip : 0u));
     }
+    if (skip_mine) return;  // uniform: the other slices learn it from the flag
+    // each wave's slot totals, for the walk, while the masses travel
+#pragma unroll
+    for (int i = 0; i < NV; ++i) slot_tot[i] = wave_sum(seg[i]);
     if (wid == 0) {
       // lane 2s + 0..1: halves of slice s's residual mass; slice s's mass to lane s
       const uint32_t v = join32(wait_tagged(row_words + kMassWord, 1, 2 * S, tag, lane, P.errword));
@@ -479,7 +502,12 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       const float v = seg_p[i] * scale;
       seg[i] = v >= kTinyMass ? v : 0.f;
     }
-    const float wt = wave_total();
+    float wt = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      slot_tot[i] = wave_sum(seg[i]);
+      wt += slot_tot[i];
+    }
     if (lane == 0) s_wt[wid] = wt;
     __syncthreads();
   }
@@ -500,8 +528,6 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   if (wstar < 0) wstar = 0;  // no positive weight (not reachable for finite inputs)
   if (wid != wstar) return;
   const float t2 = t1 - wbefore;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) slot_tot[i] = wave_sum(seg[i]);
   int istar = -1, ilast = -1;
   float icum = 0.f, ibefore = 0.f;
 #pragma unroll
@@ -568,12 +594,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   // outputs
   const uint32_t d = wait_tagged(seq_words + kDecisionWord, kSplitWordsPerRow, j, tag, lane, P.errword, dec_early);
   if (__ballot(lane < j && d != kKept) != 0) return;
-  if (lane < P.R) {
-    int tk = -1;
-    if (lane < j) tk = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * k + lane];
-    else if (lane == j) tk = y;
-    P.out_tokens[static_cast<size_t>(b) * P.R + lane] = tk;
-  }
+  if (lane < P.R) P.out_tokens[static_cast<size_t>(b) * P.R + lane] = lane < j ? tok_early : (lane == j ? y : -1);
   if (lane == 0) P.out_accept_len[b] = j;
 }
 
