@@ -124,17 +124,15 @@ __device__ __forceinline__ int pick_lane(float w, float incl, float t, bool& cla
   return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
 }
 
-// A 16-byte load of vector i, or of vector 0 when i is out of range, with nothing applied
-// to the result: a consumer in the same branch would make the wave wait for the load there.
-__device__ __forceinline__ Vec16 ld16_raw(const SV_GLOBAL Vec16* p, int i, int n) {
-  const SV_GLOBAL Vec16& g = p[static_cast<unsigned>(i) < static_cast<unsigned>(n) ? i : 0];
-  Vec16 v;
-  v.w[0] = g.w[0];
-  v.w[1] = g.w[1];
-  v.w[2] = g.w[2];
-  v.w[3] = g.w[3];
-  return v;
+// Copies vector i (vector 0 when i is out of range) of every lane straight into LDS, at
+// lds + 16 * lane (lds the same for the whole wave): no register holds the bytes in flight.
+// The wave must wait for its vector-memory count before reading them.
+__device__ __forceinline__ void ld16_to_lds(const SV_GLOBAL Vec16* p, int i, int n, Vec16* lds) {
+  __builtin_amdgcn_global_load_lds(p + (static_cast<unsigned>(i) < static_cast<unsigned>(n) ? i : 0),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum (gfx9 encoding)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x70 | 0xf00); }
 
 // Inclusive prefix sums over lanes 0..7 (valid in those lanes; the slices of a row and the
 // waves of a workgroup are at most 8).
@@ -186,6 +184,9 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   // before it; clamp: t lay past the total
   __shared__ float s_t, s_before;
   __shared__ int s_cand, s_skip, s_skipmine, s_win, s_clamp, s_fromp;
+  // a rejected row's draft vectors, when read in vectors: wave w's vector i of lane l at
+  // [(w * NV + i) * 64 + l] (kept out of registers, which hold the row's weights)
+  __shared__ Vec16 s_q[QMODE == kQVecS ? NT * NV : 1];
   __shared__ uint64_t s_gen;
 
   const int tid = threadIdx.x;
@@ -263,17 +264,20 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   const bool own_any = tm != -INFINITY;  // any element of this thread's share is above -inf
   const float ref = own_any ? tm : 0.f;
   float ts = 0.f;
-  float seg_p[NV];  // per vector: sum of 2^((l - ref) c), kept for a draw from p
+  // per element 2^((l - ref) c), against this thread's own maximum: every later weight is
+  // this times one factor, so the residual and the walks need no exponential of their own
+  float ev[NV][VE];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     float vs = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) vs += fast_exp2((E::at(buf[i], e) - ref) * c);
-    seg_p[i] = vs;
+    for (int e = 0; e < VE; ++e) {
+      ev[i][e] = fast_exp2((E::at(buf[i], e) - ref) * c);
+      vs += ev[i][e];
+    }
     ts += vs;
   }
   wave_merge_max_sum(tm, ts, c);
-  pin_packed(buf);
   if (lane == 0) {
     s_wm[wid] = tm;
     s_ws[wid] = ts;
@@ -289,14 +293,18 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   const uint64_t gen = s_gen;
   // never 0, so a zeroed word is never current; (gen + 1) < 2^37 for any realistic run
   const uint64_t tag = (((gen + 1) & ((1ull << 37) - 1)) << 11) | static_cast<uint64_t>(b & 2047);
-  if (publisher) {
-    float m_s = -INFINITY, z_s = 0.f;
-    for (int w = 0; w < NW; ++w) merge_max_sum(m_s, z_s, s_wm[w], s_ws[w], c);
-    put32(row_words + kPairWord + 4 * slice, tag, __float_as_uint(m_s));
-    put32(row_words + kPairWord + 4 * slice + 2, tag, __float_as_uint(z_s));
-    if (slice == 0) {
-      put32(row_words + kPairWord + 4 * S, tag, __float_as_uint(u_acc));
-      put32(row_words + kPairWord + 4 * S + 2, tag, __float_as_uint(u_smp));
+  if (wid == NW - 1) {
+    // the slice's pair: the waves' pairs (lane w: wave w) merged across lanes
+    float m_s = lane < NW ? s_wm[lane < NW ? lane : 0] : -INFINITY;
+    float z_s = lane < NW ? s_ws[lane < NW ? lane : 0] : 0.f;
+    merge_pairs8(m_s, z_s, c);
+    if (publisher) {
+      put32(row_words + kPairWord + 4 * slice, tag, __float_as_uint(m_s));
+      put32(row_words + kPairWord + 4 * slice + 2, tag, __float_as_uint(z_s));
+      if (slice == 0) {
+        put32(row_words + kPairWord + 4 * S, tag, __float_as_uint(u_acc));
+        put32(row_words + kPairWord + 4 * S + 2, tag, __float_as_uint(u_smp));
+      }
     }
   }
   if (tid == 0) {
@@ -362,15 +370,16 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   const bool resid_row = cand && j < k;
 
   // Memory reads first, then the stores: a wave's wait for a read also waits for whatever
-  // it issued before it.  The draft vectors are used as loaded: where a vector lies past
-  // this slice's share, or an element outside the row, the logit is -inf and the residual
-  // weight max(0, 0 - q) is 0 whatever q holds (a probability of this row or the next).
-  Vec16 qv[(QMODE == kQVecS) ? NV : 1];
+  // it issued before it.  The draft vectors go straight to LDS and are used as loaded:
+  // where a vector lies past this slice's share, or an element outside the row, the logit
+  // is -inf and the residual weight max(0, 0 - q) is 0 whatever q holds (a probability of
+  // this row or the next).
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
   if (resid_row && QMODE == kQVecS) {
     const uintptr_t qa = reinterpret_cast<uintptr_t>(qrowp);
     const SV_GLOBAL Vec16* vq = gptr<Vec16>(reinterpret_cast<const void*>(qa - (qa & 15)));
 #pragma unroll
-    for (int i = 0; i < NV; ++i) qv[i] = ld16_raw(vq, v0 + i * kWave, vend);
+    for (int i = 0; i < NV; ++i) ld16_to_lds(vq, v0 + i * kWave, vend, &s_q[(wid_u * NV + i) * kWave]);
   }
   // the decisions of the sequence's earlier rows (lane l: row l), read by every wave now so
   // that whichever wave draws the token finds them in its registers
@@ -406,22 +415,24 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
 
   float seg[NV];
   float slot_tot[NV];
-  const float invZ = 1.0f / Z;
-  // residual weights of one vector: max(0, 2^((l - m) c) / Z - q); qvec is its draft
-  // vector when the draft row is read in vectors
-  auto resid_weights = [&](const Vec16& lv, const Vec16& qvec, int vi, float* w) {
+  // 2^((l - m) c) = 2^((l - ref) c) * scale; a thread whose share is all -inf has no weight
+  const float scale = own_any ? fast_exp2((ref - m) * c) : 0.f;
+  const float scale_z = scale / Z;
+  // residual weights of one vector: max(0, p - q) with p = 2^((l - m) c) / Z; qvec is its
+  // draft vector when the draft row is read in vectors
+  auto resid_weights = [&](const float* evi, const Vec16& qvec, int vi, float* w) {
     const int e0 = vi * VE - h;
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       float q;
       if (QMODE == kQVecS) q = E::at(qvec, e);
       else q = (vi < vend && e0 + e >= 0 && e0 + e < V) ? load_elem(qrowp, e0 + e, P.q_bf16 != 0) : 0.f;
-      w[e] = fmaxf(0.f, fmaf(fast_exp2((E::at(lv, e) - m) * c), invZ, -q));
+      w[e] = fmaxf(0.f, fmaf(evi[e], scale_z, -q));
     }
   };
-  auto p_weights = [&](const Vec16& lv, float* w) {
+  auto p_weights = [&](const float* evi, float* w) {
 #pragma unroll
-    for (int e = 0; e < VE; ++e) w[e] = fast_exp2((E::at(lv, e) - m) * c);
+    for (int e = 0; e < VE; ++e) w[e] = evi[e] * scale;
   };
   // the wave's total of seg[] in one reduction, so that the mass goes out first; the slot
   // totals follow while it travels and may differ from their sum in the last bits, which
@@ -438,10 +449,11 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     // rejection stands down once any of its slices has seen an earlier one: that slice
     // flags its mass word and ends, the others end on reading the flag.  The slices
     // compute their masses meanwhile rather than wait for the word they read.
+    if (QMODE == kQVecS) wait_vmem_all();  // this wave's draft vectors are in LDS
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float w[VE];
-      resid_weights(buf[i], qv[QMODE == kQVecS ? i : 0], v0 + i * kWave, w);
+      resid_weights(ev[i], QMODE == kQVecS ? s_q[(wid * NV + i) * kWave + lane] : Vec16{}, v0 + i * kWave, w);
       float sg = 0.f;
 #pragma unroll
       for (int e = 0; e < VE; ++e) sg += w[e];
@@ -452,10 +464,9 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     if (tid == 0) s_skipmine = (rej_seen >> 8) == gen && static_cast<int>(rej_seen & 0xff) > 64 - j;
     __syncthreads();
     const bool skip_mine = s_skipmine != 0;
-    if (publisher) {
-      float mass = 0.f;
-      for (int w = 0; w < NW; ++w) mass += s_wt[w];
-      put32(row_words + kMassWord + 2 * slice, tag, __float_as_uint(mass) | (skip_mine ? kMassSkip : 0u));
+    if (wid == NW - 1) {
+      const float mass = lane_value(scan8(lane < NW ? s_wt[lane < NW ? lane : 0] : 0.f), 7);
+      if (publisher) put32(row_words + kMassWord + 2 * slice, tag, __float_as_uint(mass) | (skip_mine ? kMassSkip : 0u));
     }
     if (skip_mine) return;  // uniform: the other slices learn it from the flag
     // each wave's slot totals, for the walk, while the masses travel
@@ -493,13 +504,15 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   bool clamp = s_clamp != 0;
   if (winner != slice) return;  // uniform
   if (from_p) {
-    // this slice's vector sums of p against the row maximum: pass 1's sums, rescaled from
-    // each thread's own reference; a vector whose sum is below kTinyMass is left out, so
-    // that a vector taken holds an element whose own weight is a normal number
-    const float scale = own_any ? fast_exp2((ref - m) * c) : 0.f;
+    // this slice's vector sums of p against the row maximum; a vector whose sum is below
+    // kTinyMass is left out, so that a vector taken holds an element whose own weight is a
+    // normal number
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const float v = seg_p[i] * scale;
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) v += ev[i][e];
+      v *= scale;
       seg[i] = v >= kTinyMass ? v : 0.f;
     }
     float wt = 0.f;
@@ -547,14 +560,20 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   // the chosen slot's values, selected with compile-time indices (a run-time index into a
   // register array would move it to scratch memory)
   float sg = 0.f;
-  Vec16 ls = buf[0];
-  Vec16 qs = qv[0];
+  float es[VE];
+
+#pragma unroll
+  for (int e = 0; e < VE; ++e) es[e] = ev[0][e];
+#pragma unroll
+  for (int i = 1; i < NV; ++i)
+    if (i == istar) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) es[e] = ev[i][e];
+    }
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     if (i == istar) {
       sg = seg[i];
-      ls = buf[i];
-      if (QMODE == kQVecS) qs = qv[i];
     }
   const float scan = wave_inclusive_scan(sg);
   const float t3 = t2 - ibefore;
@@ -572,8 +591,8 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   if (lane == lstar) {
     const int vi = v0 + istar * kWave;
     float w[VE];
-    if (from_p) p_weights(ls, w);
-    else resid_weights(ls, qs, vi, w);
+    if (from_p) p_weights(es, w);
+    else resid_weights(es, QMODE == kQVecS ? s_q[(wid * NV + istar) * kWave + lane] : Vec16{}, vi, w);
     const float t4 = t3 - (lstar > 0 ? excl : 0.f);
     int ye = -1, ylast = -1;
     float ec = 0.f;
