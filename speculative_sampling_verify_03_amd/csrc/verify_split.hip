@@ -77,9 +77,10 @@ __device__ __forceinline__ void put32(uint64_t* p, uint64_t tag, uint32_t v) {
 // Called by every lane of a wave: lane l < n waits until word base[l * stride] carries
 // `tag` and returns that word's 16-bit payload (lanes >= n return 0).  `first` is a value
 // of the word read earlier (0 if none).  One read in flight at a time: a read still in
-// flight when the wait ends would hold up the wave's next wait for memory by a round trip.
-// The waves that poll are not the ones that publish, for the same reason: a wave's wait
-// for a read also waits for its own earlier stores.
+// flight when the wait ends would hold up the wave's next wait for memory (and two reads
+// in flight saw the word no sooner: its write, not the polling, sets the pace).  The waves
+// that poll are not the ones that publish, for the same reason: a wave's wait for a read
+// also waits for its own earlier stores.
 __device__ uint32_t wait_tagged(uint64_t* base, int stride, int n, uint64_t tag, int lane, uint32_t* err,
                                 uint64_t first = 0) {
   const bool mine = lane < n;
@@ -134,21 +135,22 @@ __device__ __forceinline__ void ld16_to_lds(const SV_GLOBAL Vec16* p, int i, int
 // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum (gfx9 encoding)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x70 | 0xf00); }
 
-// Inclusive prefix sums over lanes 0..7 (valid in those lanes; the slices of a row and the
-// waves of a workgroup are at most 8).
-__device__ __forceinline__ float scan8(float x) {
-  x += dpp_f<kDppShr1>(0.f, x);
-  x += dpp_f<kDppShr2>(0.f, x);
-  x += dpp_f<kDppShr4>(0.f, x);
+// Inclusive prefix sums over lanes 0..n-1, n <= 8 (valid in those lanes; the slices of a
+// row and the waves of a workgroup are at most 8); n is the same for the whole wave.
+__device__ __forceinline__ float scan8(float x, int n = 8) {
+  if (n > 1) x += dpp_f<kDppShr1>(0.f, x);
+  if (n > 2) x += dpp_f<kDppShr2>(0.f, x);
+  if (n > 4) x += dpp_f<kDppShr4>(0.f, x);
   return x;
 }
-// The (max, sum) pairs of lanes 0..7 merged (the same order wherever it runs), in every lane.
-__device__ __forceinline__ void merge_pairs8(float& m, float& s, float c) {
-  merge_step<kDppShr1>(m, s, c);
-  merge_step<kDppShr2>(m, s, c);
-  merge_step<kDppShr4>(m, s, c);
-  m = lane_value(m, 7);
-  s = lane_value(s, 7);
+// The (max, sum) pairs of lanes 0..n-1 (n <= 8, the same for the whole wave) merged, in
+// every lane: the order depends on n alone, so every slice of a row gets the same bits.
+__device__ __forceinline__ void merge_pairs8(float& m, float& s, float c, int n = 8) {
+  if (n > 1) merge_step<kDppShr1>(m, s, c);
+  if (n > 2) merge_step<kDppShr2>(m, s, c);
+  if (n > 4) merge_step<kDppShr4>(m, s, c);
+  m = lane_value(m, n - 1);
+  s = lane_value(s, n - 1);
 }
 
 template <bool BF16>
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     // the slice's pair: the waves' pairs (lane w: wave w) merged across lanes
     float m_s = lane < NW ? s_wm[lane < NW ? lane : 0] : -INFINITY;
     float z_s = lane < NW ? s_ws[lane < NW ? lane : 0] : 0.f;
-    merge_pairs8(m_s, z_s, c);
+    merge_pairs8(m_s, z_s, c, NW);
     if (publisher) {
       put32(row_words + kPairWord + 4 * slice, tag, __float_as_uint(m_s));
       put32(row_words + kPairWord + 4 * slice + 2, tag, __float_as_uint(z_s));
@@ -315,14 +317,31 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
                                    __HIP_MEMORY_SCOPE_AGENT);
   }
   // Wave 0 polls, merges the pairs (a lane-parallel merge: the same order in every slice,
-  // so all of them hold bit-identical (m, Z)), takes the acceptance decision (lane 0 =
-  // thread 0, which holds the draft token's gathered values) and, for a draw from p, picks
-  // the slice from the pairs rescaled to the row maximum.  Its picks stay in its registers
-  // for a residual that turns out empty.
+  // so all of them hold bit-identical (m, Z)) and takes the acceptance decision (lane 0 =
+  // thread 0, which holds the draft token's gathered values).  For the last row it also
+  // picks the slice of the draw from p; a rejected row picks it only if its residual
+  // turns out empty.
   double g_e = 0.0;
-  float u_smp_w = 0.f, fp_t = 0.f, fp_before = 0.f;
-  int fp_win = -1;
-  bool fp_clamp = false;
+  float u_smp_w = 0.f, pm = -INFINITY, ps = 0.f, mr = -INFINITY;
+  // a draw from p: slice masses against the row maximum, in lane s.  A slice whose mass is
+  // below twice kTinyMass per vector it holds is left out, so that a slice taken holds a
+  // vector that is not left out below.  Lane 0 posts the pick.
+  auto pick_from_p = [&]() {
+    float ms = lane < S ? ps * fast_exp2((pm - mr) * c) : 0.f;
+    if (ms < 2.f * kTinyMass * static_cast<float>(NT * NV)) ms = 0.f;
+    const float incl = scan8(ms, S);
+    const float tt = u_smp_w * lane_value(incl, S - 1);
+    bool cl = false;
+    float bef = 0.f;
+    const int win = pick_lane(ms, incl, tt, cl, bef);
+    if (lane == 0) {
+      s_fromp = 1;
+      s_win = win;
+      s_t = tt;
+      s_before = bef;
+      s_clamp = cl;
+    }
+  };
   if (wid == 0) {
     // lane 4s + 0..3: halves of slice s's max, then of its sum; lanes 4S + 0..3: halves of
     // the two uniforms
@@ -333,10 +352,11 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     // slice s's pair to lane s (every lane takes part in the shuffles)
     const uint32_t gm = static_cast<uint32_t>(__shfl(static_cast<int>(v), (4 * lane) & (kWave - 1)));
     const uint32_t gz = static_cast<uint32_t>(__shfl(static_cast<int>(vz), (4 * lane) & (kWave - 1)));
-    const float pm = lane < S ? __uint_as_float(gm) : -INFINITY;
-    const float ps = lane < S ? __uint_as_float(gz) : 0.f;
-    float mr = pm, zr = ps;
-    merge_pairs8(mr, zr, c);
+    pm = lane < S ? __uint_as_float(gm) : -INFINITY;
+    ps = lane < S ? __uint_as_float(gz) : 0.f;
+    mr = pm;
+    float zr = ps;
+    merge_pairs8(mr, zr, c, S);
     // acceptance test: u * q(x) < p(x) = e / Z with e = exp((l_x - m) / T) in float64,
     // compared as u * q(x) * Z < e so that no division sits on the path to the decision
     bool acc = false;
@@ -344,24 +364,12 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       if (g_valid) g_e = exp((static_cast<double>(g_l) - static_cast<double>(mr)) * P.invT);
       acc = g_valid && (static_cast<double>(u_acc_w) * static_cast<double>(g_q) * static_cast<double>(zr) < g_e);
     }
-    // a draw from p: slice masses against the row maximum.  A slice whose mass is below
-    // twice kTinyMass per vector it holds is left out, so that a slice taken holds a
-    // vector that is not left out below.
-    float ms = lane < S ? ps * fast_exp2((pm - mr) * c) : 0.f;
-    if (ms < 2.f * kTinyMass * static_cast<float>(NT * NV)) ms = 0.f;
-    const float incl = scan8(ms);
-    fp_t = u_smp_w * lane_value(incl, 7);
-    fp_win = pick_lane(ms, incl, fp_t, fp_clamp, fp_before);
+    if (j == k) pick_from_p();
     if (lane == 0) {
       s_m = mr;
       s_Z = zr;
       s_cand = (j == k) || !acc;
       s_skip = 0;
-      s_fromp = 1;
-      s_win = fp_win;
-      s_t = fp_t;
-      s_before = fp_before;
-      s_clamp = fp_clamp;
     }
   }
   __syncthreads();
@@ -465,7 +473,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
     __syncthreads();
     const bool skip_mine = s_skipmine != 0;
     if (wid == NW - 1) {
-      const float mass = lane_value(scan8(lane < NW ? s_wt[lane < NW ? lane : 0] : 0.f), 7);
+      const float mass = lane_value(scan8(lane < NW ? s_wt[lane < NW ? lane : 0] : 0.f, NW), NW - 1);
       if (publisher) put32(row_words + kMassWord + 2 * slice, tag, __float_as_uint(mass) | (skip_mine ? kMassSkip : 0u));
     }
     if (skip_mine) return;  // uniform: the other slices learn it from the flag
@@ -478,22 +486,24 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
       const bool any_skip = __ballot(lane < 2 * S && (lane & 1) == 0 && (v & kMassSkip)) != 0;
       const uint32_t g = static_cast<uint32_t>(__shfl(static_cast<int>(v), (2 * lane) & (kWave - 1)));
       const float mass = lane < S ? __uint_as_float(g & ~kMassSkip) : 0.f;
-      const float incl = scan8(mass);
-      const float tot = lane_value(incl, 7);
-      bool cl = false;
-      float bef = 0.f;
-      const float tt = u_smp_w * tot;
-      const int win = tot > 0.f ? pick_lane(mass, incl, tt, cl, bef) : -1;
-      if (lane == 0) {
-        s_skip = any_skip;
-        if (win >= 0) {  // else the residual is empty through rounding: the draw from p stands
+      const float incl = scan8(mass, S);
+      const float tot = lane_value(incl, S - 1);
+      if (tot > 0.f) {
+        bool cl = false;
+        float bef = 0.f;
+        const float tt = u_smp_w * tot;
+        const int win = pick_lane(mass, incl, tt, cl, bef);
+        if (lane == 0) {
           s_fromp = 0;
           s_win = win;
           s_t = tt;
           s_before = bef;
           s_clamp = cl;
         }
+      } else {
+        pick_from_p();  // the residual is empty through rounding: draw from p itself
       }
+      if (lane == 0) s_skip = any_skip;
     }
     __syncthreads();
     if (s_skip) return;  // uniform: an earlier row rejected, this row's token is not needed
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(NT) void row_split_kernel(SplitParams P) {
   int wstar;
   {
     const float wv = lane < NW ? s_wt[lane < NW ? lane : 0] : 0.f;
-    wstar = pick_lane(wv, scan8(wv), t1, clamp, wbefore);
+    wstar = pick_lane(wv, scan8(wv, NW), t1, clamp, wbefore);
   }
   if (wstar < 0) wstar = 0;  // no positive weight (not reachable for finite inputs)
   if (wid != wstar) return;
