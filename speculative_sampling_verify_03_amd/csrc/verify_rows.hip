@@ -398,14 +398,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       }
     };
     // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total.  With
-    // `slots`, also each slot's total over the wave (slot_tot[], the last lane of the slot's
-    // scan), the wave's total being their sequential sum: the search below walks exactly
-    // these sums, so every level of the inverse CDF agrees with the level above it.  Tiles
+    // `slots`, the wave's total is the sequential sum of each slot's total over the wave
+    // (slot_total(i), the last lane of the slot's scan): the search below walks exactly
+    // these sums, computed again there (same inputs, same bits) rather than held, so every
+    // level of the inverse CDF agrees with the level above it.  Tiles
     // whose totals only enter the unit weights skip the per-slot scans.  A tile that is not
     // in registers (`reload_row`) is re-read together with its first batch of q vectors, so
     // the two reads share one round trip.
     float seg[NV];
-    float slot_tot[NV];
+    auto slot_total = [&](int i) -> float { return lane_value(wave_inclusive_scan(seg[i]), 63); };
     auto tile_totals = [&](int v0, bool reload_row, bool slots) -> float {
       constexpr int GQ = QMODE == kQElem ? 2 : (NT >= 512 && QMODE == kQVec) ? 8 : NV;
       constexpr int G = NV < GQ ? NV : GQ;
@@ -444,8 +445,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       if (slots) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          slot_tot[i] = lane_value(wave_inclusive_scan(seg[i]), 63);
-          wt += slot_tot[i];
+          wt += slot_total(i);
         }
       } else {
         float own = 0.f;
@@ -478,7 +478,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         int tile;
         bool active;
         if (step < P.ntiles) {
-          tile = (first + step) % P.ntiles;
+          tile = first + step;  // (first + step) mod ntiles, both below ntiles
+          if (tile >= P.ntiles) tile -= P.ntiles;
           active = resid || (masked && unit_has_child(tile * NW + wid));
         } else {
           // a single-tile rejected row's deferred check: an earlier rejection posted
@@ -557,8 +558,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         float icum = 0.f, ibefore = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          const float nc = icum + slot_tot[i];
-          if (slot_tot[i] > 0.f) ilast = i;
+          const float st = slot_total(i);
+          const float nc = icum + st;
+          if (st > 0.f) ilast = i;
           if (!clamp && istar < 0 && static_cast<double>(nc) > t1) {
             istar = i;
             ibefore = icum;
