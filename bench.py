@@ -591,7 +591,7 @@ def main():
         tflops = wl.gemm_flops() / (ms_gemm * 1e-3) / 1e12
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name),
-                    "kernel": "lmhead_gemm_kernel", "kernel_ms": round(ms_gemm, 4),
+                    "kernel": "lmhead_gemm_dma_kernel", "kernel_ms": round(ms_gemm, 4),
                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
         extra["verify_ms"] = round(ms_verify, 4)
     else:
