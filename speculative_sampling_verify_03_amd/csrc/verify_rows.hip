@@ -75,6 +75,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   float* s_ps = s_dyn + nunits;
   float* s_tot = s_dyn + 2 * nunits;
   __shared__ int s_flag, s_y, s_last, s_skip;
+  __shared__ float s_slot[NV];    // a cooperatively recomputed unit's slot totals
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
   constexpr bool LOSSLESS = TREE && QMODE == kQLossless;
@@ -356,6 +357,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         }
       }
     };
+    // the VE mask bits of vector vi alone
+    auto vec_excl = [&](int vi) -> uint32_t {
+      uint32_t xb = 0u;
+      for (int ci = 0; ci < nx; ++ci) {
+        const int pos = s_xtok[ci] + h;
+        if (pos / VE == vi) xb |= 1u << (pos - (pos / VE) * VE);
+      }
+      return xb;
+    };
     // the VE mask bits of slot i (i known at compile time in the tile loops)
     auto slot_bits = [&](const uint32_t (&em)[kMaskWords], int i) -> uint32_t {
       return (em[(i * VE) / 32] >> ((i * VE) & 31)) & ((1u << VE) - 1u);
@@ -462,7 +472,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       // of every tile (residual draws only; the register-resident tile first, the others
       // re-read, mostly from cache); the last step locates the winning (tile, wave) and lets
       // that wave recompute its sums when they are not in registers already.
-      bool empty = false, skip = false;
+      bool empty = false, skip = false, coop = false;
       double t = 0.0, before = 0.0;
       bool clamp = false;
       int tile_s = 0, wave_s = 0;
@@ -531,7 +541,11 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           tile_s = star / NW;
           wave_s = star - tile_s * NW;
           tile = tile_s;
-          active = (wid == wave_s) && (tile_s != loaded_tile || !resid);
+          // The winning unit's weights are recomputed by every wave together (a quarter or an
+          // eighth of its slots each; the unit is reloaded, from cache when it is the tile in
+          // registers) unless a residual draw already holds them in the winner's registers.
+          coop = !resid || tile_s != loaded_tile;
+          active = false;
         }
         if (active) {
           const int v0 = tile * TILE + wid * (NV * kWave) + lane;
@@ -550,7 +564,93 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         wsc = 1.0f;
         continue;
       }
-      if (wid == wave_s) {
+      if (coop) {
+        // wave w reloads slots [w * NS, (w + 1) * NS) of the unit, computes their weights and
+        // slot totals; the wave that owns the winning slot walks it
+        constexpr int NS = NV >= NW ? NV / NW : 1;
+        const int ubase = tile_s * TILE + wave_s * (NV * kWave) + lane;  // slot i: ubase + 64 i
+        const bool owns = wid * NS < NV;
+        Vec16 cl[NS], cq[NS];
+        float cs[NS];
+#pragma unroll
+        for (int ii = 0; ii < NS; ++ii) cl[ii] = ld16_any(vrow, ubase + (wid * NS + ii) * kWave, owns ? nvec : 0);
+#pragma unroll
+        for (int ii = 0; ii < NS; ++ii) cq[ii] = load_q(owns ? ubase + (wid * NS + ii) * kWave : nvec);
+#pragma unroll
+        for (int ii = 0; ii < NS; ++ii) {
+          const int vi = ubase + (wid * NS + ii) * kWave;
+          cl[ii] = mask_edges<BF16>(cl[ii], vi * VE - h, V);
+          float w[VE];
+          weights(cl[ii], cq[ii], vi, w, masked ? vec_excl(vi) : 0u);
+          float sg = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) sg += w[e];
+          cs[ii] = owns ? sg : 0.f;
+          const float st = wave_sum(cs[ii]);
+          if (owns && lane == 0) s_slot[wid * NS + ii] = st;
+        }
+        __syncthreads();
+        // slot inside the unit (uniform walk over the slot totals)
+        const double t1 = t - before;
+        int istar = -1, ilast = -1;
+        float icum = 0.f, ibefore = 0.f;
+        for (int i = 0; i < NV; ++i) {
+          const float st = s_slot[i];
+          const float nc = icum + st;
+          if (st > 0.f) ilast = i;
+          if (!clamp && istar < 0 && static_cast<double>(nc) > t1) {
+            istar = i;
+            ibefore = icum;
+          }
+          icum = nc;
+        }
+        if (istar < 0) {
+          istar = ilast < 0 ? 0 : ilast;
+          clamp = true;
+        }
+        if (wid == istar / NS) {
+          const int ii0 = istar - wid * NS;
+          float sg = 0.f;
+          Vec16 ls = cl[0], qs = cq[0];
+#pragma unroll
+          for (int ii = 0; ii < NS; ++ii)
+            if (ii == ii0) {
+              sg = cs[ii];
+              ls = cl[ii];
+              qs = cq[ii];
+            }
+          const int vi = ubase + istar * kWave;
+          const float scan = wave_inclusive_scan(sg);
+          const double t2 = t1 - static_cast<double>(ibefore);
+          const uint64_t hit = __ballot(sg > 0.f && static_cast<double>(scan) > t2);
+          const uint64_t pos = __ballot(sg > 0.f);
+          int lstar;
+          if (!clamp && hit) {
+            lstar = __ffsll(static_cast<long long>(hit)) - 1;
+          } else {
+            lstar = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+            clamp = true;
+          }
+          const float excl = lane_value(scan, lstar > 0 ? lstar - 1 : 0);
+          if (lane == lstar) {
+            float w[VE];
+            weights(ls, qs, vi, w, masked ? vec_excl(vi) : 0u);
+            const double t3 = t2 - (lstar > 0 ? static_cast<double>(excl) : 0.0);
+            int y = -1, ylast = -1;
+            float ec = 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+              ec += w[e];
+              if (w[e] > 0.f) {
+                ylast = e;
+                if (!clamp && y < 0 && static_cast<double>(ec) > t3) y = e;
+              }
+            }
+            if (y < 0) y = ylast < 0 ? 0 : ylast;
+            s_y = vi * VE - h + y;
+          }
+        }
+      } else if (wid == wave_s) {
         const int v0 = tile_s * TILE + wid * (NV * kWave) + lane;
         // slot inside the wave (uniform walk over the slot totals)
         const double t1 = t - before;
