@@ -95,6 +95,9 @@ int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* p
   const bool bf16 = (lt == SV_BF16);
   const sv::RowConfig rc = sv::choose_row_config(bf16, V, head_max(logits, V, lt), static_cast<int64_t>(B) * R);
   P.ntiles = rc.ntiles;
+  P.errword = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.status_off);
+  P.help_words = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.help_off);
+  P.help_stride = sv::help_stride(V);
   sv::TreeDesc td{};
   if (tree) {
     std::memcpy(td.parent, ti->parent, 64);
@@ -149,6 +152,12 @@ int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* p
     const hipError_t e = sv::launch_split(S, bf16, qmode == 1 ? 1 : 0, sc, st);
     return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
   }
+  // A rejected row walked in tiles gets help from the later rows of its sequence when a
+  // row's units fit one wave's lanes (the row waits for the tiles its helpers claimed;
+  // a helper claims only while it runs, so no wait depends on a workgroup not yet started).
+  const int64_t rows = static_cast<int64_t>(B) * R;
+  P.help_on = !tree && k > 0 && rc.ntiles > 1 && rows <= sv::kHelpRows && rc.ntiles * (rc.threads / 64) <= 64 &&
+              rc.ntiles * (rc.threads / 64) + 3 <= P.help_stride;
   const hipError_t e = sv::launch_rows(P, td, bf16, tree, qmode, rc.cfg, B * R, st);
   return e == hipSuccess ? SV_OK : SV_E_LAUNCH;
 }

@@ -30,7 +30,14 @@ struct RowParams {
                            //     candidate, and 64 - row of the earliest rejection seen;
                            //     tree: mask of accepted nodes (word 0)
   uint64_t* rowword;       // [B * R] tree: candidate token + 1 of each node
-  // every word above is zero on entry and is returned to zero before the kernel ends
+  // Linear multi-tile rows (help_on): the rows after a sequence's earliest rejection
+  // compute residual tiles of that rejected row (verify_rows.hip).
+  uint64_t* help_words;    // per row help_stride words: (m, Z), tile claims, unit totals
+  int32_t help_stride;
+  int32_t help_on;
+  uint32_t* errword;       // sticky: set when a wait for another workgroup ran out
+  // every word above except errword is zero on entry and is returned to zero before the
+  // kernel ends
 };
 
 // Static tree, BFS order, at most 64 nodes; passed by value in the kernel arguments.
@@ -55,7 +62,7 @@ RowConfig choose_row_config(bool bf16, int V, int head_max, int64_t rows);
 hipError_t launch_rows(const RowParams& P, const TreeDesc& td, bool bf16, bool tree, int qmode, int cfg,
                        int grid, hipStream_t st);
 
-// Linear kernel with each row split over S co-resident workgroups (cooperative launch):
+// Linear kernel with each row split over S co-resident workgroups:
 // at most kSplitSlices slices per row, at most kSplitRows rows (the workspace holds slots
 // for those; validate.hpp).
 constexpr int kSplitShapeCount = 4;   // (threads, vectors per thread) instances

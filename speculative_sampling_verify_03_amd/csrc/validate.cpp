@@ -61,7 +61,10 @@ bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H,
   out->counters_off = out->words_off + round_up(splits * kSplitWordsPerRow * w);
   out->seq_off = out->counters_off + round_up(b * sizeof(uint32_t));
   out->row_off = out->seq_off + round_up(2 * b * w);
-  out->total = out->row_off + round_up(rows * w);
+  out->help_off = out->row_off + round_up(rows * w);
+  const bool linear = kind == SV_KIND_LINEAR || kind == SV_KIND_LMHEAD;
+  const size_t hrows = linear ? (rows < static_cast<size_t>(kHelpRows) ? rows : static_cast<size_t>(kHelpRows)) : 0;
+  out->total = out->help_off + round_up(hrows * static_cast<size_t>(help_stride(V)) * w);
   return true;
 }
 

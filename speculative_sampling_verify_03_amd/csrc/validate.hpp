@@ -19,17 +19,25 @@ constexpr size_t kWsAlign = 256;
 // read as anything else by a later call of any kind (they carry tags no later call will
 // look for).  After it come the sections of the row, greedy and tree kernels, which they
 // return to zero before they end: arrival counters u32[B], per-sequence words u64[B][2],
-// per-row words u64[B * rows] (rows = k + 1, or N for a tree).  Sections are 256-byte
-// aligned.
+// per-row words u64[B * rows] (rows = k + 1, or N for a tree), and for linear kinds the
+// help section described below.  Sections are 256-byte aligned.
 constexpr int64_t kSplitRows = 2048;
 constexpr int kSplitSlices = 8;
 // per row: (max, sum) pair of each slice (4 words), the row's two uniforms (4 words),
 // residual mass of each slice (2 words), the row's decision (1 word)
 constexpr int kSplitWordsPerRow = 6 * kSplitSlices + 5;
 
+// Linear rows drawn by the row kernel in tiles can be helped by the later rows of their
+// sequence (residual tiles computed there) when the launch has at most kHelpRows rows.
+// The help section holds per row help_stride(V) u64 words: its (max, sum), a tile claim
+// counter and one total per (tile, wave) unit.
+constexpr int64_t kHelpRows = 2048;
+inline int32_t help_stride(int32_t V) { return 2 + (V + 3) / 4096 + 9; }
+
 struct WsLayout {
   size_t status_off, gen_off, rej_off, words_off;  // fixed prefix
   size_t counters_off, seq_off, row_off;           // row kernel, greedy and tree kernels
+  size_t help_off;                                 // row kernel, linear (0 size otherwise)
   size_t total;
 };
 bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H, WsLayout* out);

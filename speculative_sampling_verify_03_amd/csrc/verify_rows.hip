@@ -40,6 +40,12 @@ namespace sv {
 // kQLossless is the lossless tree: no q rows at all (each candidate is a fixed top-K
 // token, so its draft law is a point mass).
 constexpr int kQElem = 0, kQVec = 1, kQHalf = 2, kQLossless = 3;
+constexpr int kHelpSpin = 1 << 20;  // polls before a wait on the help words gives up
+
+
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum (gfx9 encoding): this
+// wave's loads, stores and atomics have all been acknowledged
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x70 | 0xf00); }
 
 // Occupancy target: at least two waves per SIMD (up to 256 VGPRs).  Holding the
 // multi-tile 512 x 16 configurations to 128 VGPRs (two workgroups per CU) spilled the
@@ -76,9 +82,14 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   float* s_tot = s_dyn + 2 * nunits;
   __shared__ int s_flag, s_y, s_last, s_skip;
   __shared__ float s_slot[NV];    // a cooperatively recomputed unit's slot totals
+  __shared__ int s_claim[2], s_hr, s_help;  // residual tiles claimed; the row this one helps
+  __shared__ float s_hm, s_hz;                      // the helped row's (max, sum)
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
   constexpr bool LOSSLESS = TREE && QMODE == kQLossless;
+  // linear rows walked in tiles (16 vectors per thread: the single-tile shapes hold fewer)
+  // can be helped by workgroups that are done (below)
+  constexpr bool HELP = !TREE && NV == 16;
   // single-tile linear rows with q vectors in phase: the rejection check is deferred (below)
   constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
   // linear rows of several waves draw their position's pair in uniform control flow (below)
@@ -280,6 +291,10 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     // A single-tile row reads the answer only at the barrier before its unit walk, so the
     // atomic's round trip overlaps its draft-row loads and residual weights; a multi-tile
     // row, whose draw re-reads its tiles, reads it before starting.
+    if (HELP && P.help_on && rejected)  // the row's (m, Z), for the rows that may help it
+      __hip_atomic_store(P.help_words + static_cast<size_t>(r) * P.help_stride,
+                         (static_cast<uint64_t>(__float_as_uint(m)) << 32) | __float_as_uint(Z), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     {
       if (rejected) {
         if (DEFER) {
@@ -299,6 +314,27 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         if (seen > static_cast<uint64_t>(64 - j)) cand = false;
       }
     }
+    s_help = -1;
+    if (HELP && P.help_on) {
+      // Rows walked in tiles mark their decision in the sequence's mask, after publishing
+      // any rejection; a later row waits for the earlier rows' marks (they decide without
+      // waiting on anything, and start before it), then stands down if one of them
+      // rejected and helps the earliest one with its residual tiles.
+      uint64_t* dm = P.help_words + static_cast<size_t>(b * P.R) * P.help_stride + (P.help_stride - 1);
+      (void)__hip_atomic_fetch_or(dm, 1ull << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (j > 0) {
+        const uint64_t low = (1ull << j) - 1ull;
+        uint64_t v = 0;
+        for (int spin = 0; spin < kHelpSpin && (v & low) != low; ++spin)
+          v = __hip_atomic_load(dm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t seen = __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int jf = seen > 0 ? 64 - static_cast<int>(seen) : P.R;
+        if (jf < j) {
+          cand = false;
+          s_help = jf;
+        }
+      }
+    }
     s_flag = cand;
   }
   if (tid == 0) {
@@ -313,159 +349,150 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   }
   __syncthreads();
 
-  // ---- pass 2: candidate draw from this row
-  if (s_flag) {
-    const float u_smp = s_usmp;
-    const float invZ = 1.0f / Z;
-    // linear: the residual at a rejected position
-    bool resid = !TREE && (j < P.k);
-    // lossless tree: p without the children's tokens
-    bool masked = LOSSLESS && s_nx > 0;
-    const int nx = LOSSLESS ? s_nx : 0;
-    const char* qrowp = static_cast<const char*>(P.probs) +
-                        (static_cast<size_t>(b) * (TREE ? P.R : P.k) + j) * V * qeb;
-    const uintptr_t qa = reinterpret_cast<uintptr_t>(qrowp);
-    const SV_GLOBAL Vec16* vq = gptr<Vec16>(reinterpret_cast<const void*>(qa - (qa & 15)));
-
-    auto load_q = [&](int vi) -> Vec16 {
-      Vec16 v{};
-      if (QMODE == kQVec && resid) v = ld16(vq, vi, nvec);
-      if (QMODE == kQHalf && resid) {  // branch free like ld16: lanes past the row load vector 0
-        const bool in = vi < nvec;
-        const int e0 = (in ? vi : 0) * VE - h;  // 8-byte aligned in q by the host's choice of mode
-        const uint64_t d = *gptr<uint64_t>(qrowp + static_cast<ptrdiff_t>(e0) * 2);
-        v.w[0] = in ? static_cast<uint32_t>(d) : 0u;
-        v.w[1] = in ? static_cast<uint32_t>(d >> 32) : 0u;
+  // ---- pass 2: candidate draw from this row.  The weights and tile sums below read the
+  // row through cur_* (this row's; a helper points them at the row it helps, see below).
+  const float invZ = 1.0f / Z;
+  // linear: the residual at a rejected position
+  bool resid = !TREE && (j < P.k);
+  // lossless tree: p without the children's tokens
+  bool masked = LOSSLESS && s_nx > 0;
+  const int nx = LOSSLESS ? s_nx : 0;
+  const SV_GLOBAL Vec16* cur_vrow = vrow;
+  int cur_nvec = nvec, cur_h = h;
+  float cur_m = m;
+  const char* qrowp = static_cast<const char*>(P.probs) +
+                      (static_cast<size_t>(b) * (TREE ? P.R : P.k) + (TREE || j < P.k ? j : 0)) * V * qeb;
+  const SV_GLOBAL Vec16* vq = gptr<Vec16>(
+      reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(qrowp) - (reinterpret_cast<uintptr_t>(qrowp) & 15)));
+  auto load_q = [&](int vi) -> Vec16 {
+    Vec16 v{};
+    if (QMODE == kQVec && resid) v = ld16(vq, vi, cur_nvec);
+    if (QMODE == kQHalf && resid) {  // branch free like ld16: lanes past the row load vector 0
+      const bool in = vi < cur_nvec;
+      const int e0 = (in ? vi : 0) * VE - cur_h;  // 8-byte aligned in q by the host's choice of mode
+      const uint64_t d = *gptr<uint64_t>(qrowp + static_cast<ptrdiff_t>(e0) * 2);
+      v.w[0] = in ? static_cast<uint32_t>(d) : 0u;
+      v.w[1] = in ? static_cast<uint32_t>(d >> 32) : 0u;
+    }
+    return v;
+  };
+  // Lossless tree: bit i * VE + e of em[] is set when element e of this thread's vector
+  // v0 + i * kWave is one of the children's tokens (rare: a vector with no bit set is
+  // never touched by the mask).
+  constexpr int kMaskWords = (NV * VE + 31) / 32;
+  auto excl_bits = [&](int v0, uint32_t (&em)[kMaskWords]) {
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) em[k] = 0u;
+    for (int ci = 0; ci < nx; ++ci) {
+      const int pos = s_xtok[ci] + h;  // element position in the vector-aligned stream
+      const int d = pos / VE - v0;
+      if (d >= 0 && d < NV * kWave && (d & (kWave - 1)) == 0) {
+        const int bit = (d / kWave) * VE + (pos - (pos / VE) * VE);
+#pragma unroll
+        for (int k = 0; k < kMaskWords; ++k)
+          if (k == bit / 32) em[k] |= 1u << (bit & 31);
       }
-      return v;
-    };
-    // Lossless tree: bit i * VE + e of em[] is set when element e of this thread's vector
-    // v0 + i * kWave is one of the children's tokens (rare: a vector with no bit set is
-    // never touched by the mask).
-    constexpr int kMaskWords = (NV * VE + 31) / 32;
-    auto excl_bits = [&](int v0, uint32_t (&em)[kMaskWords]) {
+    }
+  };
+  // the VE mask bits of vector vi alone
+  auto vec_excl = [&](int vi) -> uint32_t {
+    uint32_t xb = 0u;
+    for (int ci = 0; ci < nx; ++ci) {
+      const int pos = s_xtok[ci] + h;
+      if (pos / VE == vi) xb |= 1u << (pos - (pos / VE) * VE);
+    }
+    return xb;
+  };
+  // the VE mask bits of slot i (i known at compile time in the tile loops)
+  auto slot_bits = [&](const uint32_t (&em)[kMaskWords], int i) -> uint32_t {
+    return (em[(i * VE) / 32] >> ((i * VE) & 31)) & ((1u << VE) - 1u);
+  };
+  // Lossless tree: does unit q (tile q / NW, wave q % NW) hold one of the children's tokens?
+  auto unit_has_child = [&](int q) -> bool {
+    bool any = false;
+    for (int ci = 0; ci < nx; ++ci) {
+      const int vc = (s_xtok[ci] + h) / VE;
+      any = any || (vc / TILE) * NW + (vc % TILE) / (NV * kWave) == q;
+    }
+    return any;
+  };
+  // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
+  // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0), or
+  // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`xb`: the mask
+  // bits of this vector).  Linear rows use one form for both: max(0, x * s - q) with
+  // s = 1 / Z and q from the draft row for a residual, s = 1 and q = 0 otherwise (q
+  // vectors are zero when not loaded), which is exactly x for x >= 0, so the residual
+  // loop carries no per-element select.  Tree rows never take a residual: x itself.
+  float wsc = resid ? invZ : 1.0f;
+  auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w, uint32_t xb = 0u) {
+    const int e0 = vi * VE - cur_h;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float x = fast_exp2((E::at(lv, e) - cur_m) * c);
+      if (TREE) {
+        w[e] = x;
+        continue;
+      }
+      float q = 0.f;
+      if (QMODE == kQVec) q = E::at(qv, e);
+      else if (QMODE == kQHalf) q = Elem<true>::at(qv, e);
+      else if (resid) q = (e0 + e >= 0 && e0 + e < V) ? load_elem(qrowp, e0 + e, P.q_bf16 != 0) : 0.f;
+      w[e] = fmaxf(0.f, fmaf(x, wsc, -q));
+    }
+    if (LOSSLESS) {  // branch free: a branch here kept every vector's weights live at once
+#pragma unroll
+      for (int e = 0; e < VE; ++e) w[e] = ((xb >> e) & 1u) ? 0.f : w[e];
+    }
+  };
+  // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total (the
+  // sequential sum of seg[], then a wave reduction: the same bits whichever workgroup
+  // computes it).  The walk sums each slot over the wave (slot_total) from the same seg[].
+  // A tile that is not in registers (`reload_row`) is re-read together with its first batch
+  // of q vectors, so the two reads share one round trip.
+  float seg[NV];
+  auto slot_total = [&](int i) -> float { return lane_value(wave_inclusive_scan(seg[i]), 63); };
+  auto tile_totals = [&](int v0, bool reload_row) -> float {
+    constexpr int GQ = QMODE == kQElem ? 2 : (NT >= 512 && QMODE == kQVec) ? 8 : NV;
+    constexpr int G = NV < GQ ? NV : GQ;
+    if (reload_row) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) buf[i] = ld16_any(cur_vrow, v0 + i * kWave, cur_nvec);
+    }
+    uint32_t em[kMaskWords];
+    if (masked) excl_bits(v0, em);
+    else {
 #pragma unroll
       for (int k = 0; k < kMaskWords; ++k) em[k] = 0u;
-      for (int ci = 0; ci < nx; ++ci) {
-        const int pos = s_xtok[ci] + h;  // element position in the vector-aligned stream
-        const int d = pos / VE - v0;
-        if (d >= 0 && d < NV * kWave && (d & (kWave - 1)) == 0) {
-          const int bit = (d / kWave) * VE + (pos - (pos / VE) * VE);
+    }
 #pragma unroll
-          for (int k = 0; k < kMaskWords; ++k)
-            if (k == bit / 32) em[k] |= 1u << (bit & 31);
-        }
-      }
-    };
-    // the VE mask bits of vector vi alone
-    auto vec_excl = [&](int vi) -> uint32_t {
-      uint32_t xb = 0u;
-      for (int ci = 0; ci < nx; ++ci) {
-        const int pos = s_xtok[ci] + h;
-        if (pos / VE == vi) xb |= 1u << (pos - (pos / VE) * VE);
-      }
-      return xb;
-    };
-    // the VE mask bits of slot i (i known at compile time in the tile loops)
-    auto slot_bits = [&](const uint32_t (&em)[kMaskWords], int i) -> uint32_t {
-      return (em[(i * VE) / 32] >> ((i * VE) & 31)) & ((1u << VE) - 1u);
-    };
-    // Lossless tree: does unit q (tile q / NW, wave q % NW) hold one of the children's tokens?
-    auto unit_has_child = [&](int q) -> bool {
-      bool any = false;
-      for (int ci = 0; ci < nx; ++ci) {
-        const int vc = (s_xtok[ci] + h) / VE;
-        any = any || (vc / TILE) * NW + (vc % TILE) / (NV * kWave) == q;
-      }
-      return any;
-    };
-    // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
-    // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0), or
-    // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`xb`: the mask
-    // bits of this vector).  Linear rows use one form for both: max(0, x * s - q) with
-    // s = 1 / Z and q from the draft row for a residual, s = 1 and q = 0 otherwise (q
-    // vectors are zero when not loaded), which is exactly x for x >= 0, so the residual
-    // loop carries no per-element select.  Tree rows never take a residual: x itself.
-    float wsc = resid ? invZ : 1.0f;
-    auto weights = [&](const Vec16& lv, const Vec16& qv, int vi, float* w, uint32_t xb = 0u) {
-      const int e0 = vi * VE - h;
+    for (int g0 = 0; g0 < NV; g0 += G) {
+      Vec16 qv[G] = {};
+      if (resid) {  // one uniform branch around the whole batch of q loads
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const float x = fast_exp2((E::at(lv, e) - m) * c);
-        if (TREE) {
-          w[e] = x;
-          continue;
-        }
-        float q = 0.f;
-        if (QMODE == kQVec) q = E::at(qv, e);
-        else if (QMODE == kQHalf) q = Elem<true>::at(qv, e);
-        else if (resid) q = (e0 + e >= 0 && e0 + e < V) ? load_elem(qrowp, e0 + e, P.q_bf16 != 0) : 0.f;
-        w[e] = fmaxf(0.f, fmaf(x, wsc, -q));
+        for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
       }
-      if (LOSSLESS) {  // branch free: a branch here kept every vector's weights live at once
+      if (g0 == 0 && reload_row) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) w[e] = ((xb >> e) & 1u) ? 0.f : w[e];
-      }
-    };
-    // Per-vector sums of this thread's share of a tile (seg[]) and the wave's total.  With
-    // `slots`, the wave's total is the sequential sum of each slot's total over the wave
-    // (slot_total(i), the last lane of the slot's scan): the search below walks exactly
-    // these sums, computed again there (same inputs, same bits) rather than held, so every
-    // level of the inverse CDF agrees with the level above it.  Tiles
-    // whose totals only enter the unit weights skip the per-slot scans.  A tile that is not
-    // in registers (`reload_row`) is re-read together with its first batch of q vectors, so
-    // the two reads share one round trip.
-    float seg[NV];
-    auto slot_total = [&](int i) -> float { return lane_value(wave_inclusive_scan(seg[i]), 63); };
-    auto tile_totals = [&](int v0, bool reload_row, bool slots) -> float {
-      constexpr int GQ = QMODE == kQElem ? 2 : (NT >= 512 && QMODE == kQVec) ? 8 : NV;
-      constexpr int G = NV < GQ ? NV : GQ;
-      if (reload_row) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) buf[i] = ld16_any(vrow, v0 + i * kWave, nvec);
-      }
-      uint32_t em[kMaskWords];
-      if (masked) excl_bits(v0, em);
-      else {
-#pragma unroll
-        for (int k = 0; k < kMaskWords; ++k) em[k] = 0u;
+        for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - cur_h, V);
       }
 #pragma unroll
-      for (int g0 = 0; g0 < NV; g0 += G) {
-        Vec16 qv[G] = {};
-        if (resid) {  // one uniform branch around the whole batch of q loads
+      for (int g = 0; g < G; ++g) {
+        float w[VE];
+        weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w, LOSSLESS ? slot_bits(em, g0 + g) : 0u);
+        float sgm = 0.f;
 #pragma unroll
-          for (int g = 0; g < G; ++g) qv[g] = load_q(v0 + (g0 + g) * kWave);
-        }
-        if (g0 == 0 && reload_row) {
-#pragma unroll
-          for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float w[VE];
-          weights(buf[g0 + g], qv[g], v0 + (g0 + g) * kWave, w, LOSSLESS ? slot_bits(em, g0 + g) : 0u);
-          float sgm = 0.f;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) sgm += w[e];
-          seg[g0 + g] = sgm;
-        }
+        for (int e = 0; e < VE; ++e) sgm += w[e];
+        seg[g0 + g] = sgm;
       }
-      float wt = 0.f;
-      if (slots) {
+    }
+    float own = 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          wt += slot_total(i);
-        }
-      } else {
-        float own = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) own += seg[i];
-        wt = wave_sum(own);
-      }
-      return wt;
-    };
+    for (int i = 0; i < NV; ++i) own += seg[i];
+    return wave_sum(own);
+  };
 
+  if (s_flag) {
+    const float u_smp = s_usmp;
     int loaded_tile = P.ntiles - 1;  // buf holds the last tile of pass 1
     for (int attempt = 0; attempt < 2; ++attempt) {
       // One loop, one copy of tile_totals: steps 0 .. ntiles-1 compute the residual totals
@@ -484,7 +511,54 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         for (int q = tid; q < nunits; q += NT) s_tot[q] = -1.f;
         __syncthreads();
       }
-      for (int step = (resid || masked) ? 0 : P.ntiles; step <= P.ntiles; ++step) {
+      int step0 = (resid || masked) ? 0 : P.ntiles;
+      if (HELP && resid && P.help_on) {
+        // The residual's tiles are claimed one at a time from the row's counter, which the
+        // rows that help claim from too: the tile in registers first (never claimed), then
+        // the claimed ones (the next claim in flight while a tile is summed), then the
+        // totals of the tiles others claimed, which those workgroups publish as they finish.
+        uint64_t* hw = P.help_words + static_cast<size_t>(r) * P.help_stride;
+        uint64_t cl = 0;
+        if (tid == 0) cl = __hip_atomic_fetch_add(&hw[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        {
+          const float wt = tile_totals(loaded_tile * TILE + wid * (NV * kWave) + lane, false);
+          if (lane == 0) s_tot[loaded_tile * NW + wid] = wt;
+        }
+        if (tid == 0) s_claim[0] = static_cast<int>(cl);
+        __syncthreads();
+        uint64_t mine = 0;
+        for (int it = 0;; ++it) {
+          const int cc = s_claim[it & 1];
+          if (cc >= P.ntiles - 1) break;
+          if (tid == 0) cl = __hip_atomic_fetch_add(&hw[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float wt = tile_totals(cc * TILE + wid * (NV * kWave) + lane, true);
+          loaded_tile = cc;
+          if (lane == 0) s_tot[cc * NW + wid] = wt;
+          mine |= 1ull << cc;
+          if (tid == 0) s_claim[(it + 1) & 1] = static_cast<int>(cl);
+          __syncthreads();
+        }
+        if (wid == 0) {
+          // unit (t, w) of a tile summed elsewhere arrives in word 2 + t * NW + w (bit 32 set)
+          const bool need = lane < (P.ntiles - 1) * NW && !((mine >> (lane / NW)) & 1ull);
+          uint64_t v = 0;
+          bool have = !need;
+          for (int spin = 0;; ++spin) {
+            if (__ballot(!have) == 0) break;
+            if (spin == kHelpSpin) {
+              if (lane == 0) __hip_atomic_fetch_or(P.errword, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            if (!have) {
+              v = __hip_atomic_load(&hw[2 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              have = v != 0;
+            }
+          }
+          if (need) s_tot[lane] = __uint_as_float(static_cast<uint32_t>(v));
+        }
+        step0 = P.ntiles;  // only the unit pick is left (its barrier follows)
+      }
+      for (int step = step0; step <= P.ntiles; ++step) {
         int tile;
         bool active;
         if (step < P.ntiles) {
@@ -552,7 +626,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           const bool reload_row = tile != loaded_tile;  // only this wave's share when locating the winner
           loaded_tile = tile;
           // slot totals for the tile that stays in registers (the last step) and for the winner
-          const float wt = tile_totals(v0, reload_row, step >= P.ntiles - 1);
+          const float wt = tile_totals(v0, reload_row);
           if (step < P.ntiles && lane == 0) s_tot[tile * NW + wid] = wt;
         }
       }
@@ -731,6 +805,66 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   }
   __syncthreads();
 
+  // ---- help: a row after its sequence's earliest rejection supplies nothing to the
+  // outputs; it claims residual tiles of that rejected row (from the row's own counter,
+  // which the row claims from too) and publishes their per-wave totals (the same sums the
+  // row's own workgroup would compute: tile_totals on that row)
+  if (HELP && P.help_on) {
+    if (tid == 0) {
+      s_hr = -1;
+      if (s_help >= 0) {
+        const int hr = b * P.R + s_help;
+        uint64_t mz = 0;
+        for (int spin = 0; spin < kHelpSpin && mz == 0; ++spin)
+          mz = __hip_atomic_load(P.help_words + static_cast<size_t>(hr) * P.help_stride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (mz != 0) {
+          s_hr = hr;
+          s_hm = __uint_as_float(static_cast<uint32_t>(mz >> 32));
+          s_hz = __uint_as_float(static_cast<uint32_t>(mz));
+        }
+      }
+    }
+    __syncthreads();
+    const int hr = __builtin_amdgcn_readfirstlane(s_hr);
+    if (hr >= 0) {
+      uint64_t* hw = P.help_words + static_cast<size_t>(hr) * P.help_stride;
+      // point the weights at row hr: its residual against its own (m, Z)
+      const int hj = hr - b * P.R;
+      const char* hrowp = static_cast<const char*>(P.logits) + static_cast<size_t>(hr) * V * EB;
+      const uintptr_t hra = reinterpret_cast<uintptr_t>(hrowp);
+      cur_h = static_cast<int>(hra & 15) / EB;
+      cur_vrow = gptr<Vec16>(reinterpret_cast<const void*>(hra - (hra & 15)));
+      cur_nvec = (V + cur_h + VE - 1) / VE;
+      qrowp = static_cast<const char*>(P.probs) + (static_cast<size_t>(b) * P.k + hj) * V * qeb;
+      vq = gptr<Vec16>(reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(qrowp) -
+                                                      (reinterpret_cast<uintptr_t>(qrowp) & 15)));
+      cur_m = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(s_hm)));
+      wsc = 1.0f / __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(s_hz)));
+      resid = true;
+      masked = false;
+      if (tid == 0) s_claim[0] = static_cast<int>(__hip_atomic_fetch_add(&hw[1], 1ull, __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT));
+      __syncthreads();
+      for (int it = 0;; ++it) {
+        const int cc = s_claim[it & 1];
+        if (cc >= P.ntiles - 1) break;
+        uint64_t cl = 0;
+        if (tid == 0) cl = __hip_atomic_fetch_add(&hw[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float wt = tile_totals(cc * TILE + wid * (NV * kWave) + lane, true);
+        if (lane == 0)
+          __hip_atomic_store(&hw[2 + cc * NW + wid], (1ull << 32) | __float_as_uint(wt), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) s_claim[(it + 1) & 1] = static_cast<int>(cl);
+        __syncthreads();
+      }
+    }
+    // this workgroup's stores and atomics on the help words are acknowledged before its
+    // ticket: the sequence's last workgroup clears them afterwards
+    wait_vmem_all();
+    __syncthreads();
+  }
+
   // ---- publish this row's result, then take the sequence ticket
   if (tid == 0) {
     uint64_t dep = 0;
@@ -752,6 +886,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   if (!s_last || wid != 0) return;
 
   // ---- last arrival: the sequence's outputs
+  if (HELP && P.help_on) {  // the help words of the sequence's rows and its decision mask
+    const int per = 2 + P.ntiles * NW;
+    for (int q = lane; q < P.R * per; q += kWave)
+      __hip_atomic_store(&P.help_words[static_cast<size_t>(b * P.R + q / per) * P.help_stride + q % per], 0ull,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+      __hip_atomic_store(&P.help_words[static_cast<size_t>(b * P.R) * P.help_stride + (P.help_stride - 1)], 0ull,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (!TREE) {
     const int k = P.k;
     // the draft tokens are read while the exchange below is in flight (k = 0 reads a

@@ -150,6 +150,36 @@ def test_disjoint_supports_emit_one():
     assert np.all(got["accept_len"] == 0) and np.all(got["tokens"][:, 0] < 32)
 
 
+@pytest.mark.parametrize("lt,qt,V", [("bf16", "bf16", 70000),   # draft rows read in 16-byte vectors
+                                     ("bf16", "bf16", 70001),   # element-wise
+                                     ("f32", "bf16", 70000)])   # 8-byte bf16 chunks (LM-head path)
+def test_residual_tiles_helped_by_later_rows(lt, qt, V):
+    # Position 0 always rejects (disjoint supports): its residual is p_0 itself, over rows
+    # walked in tiles (960 rows keep the batch off the split kernel).  The later rows of
+    # each sequence stand down and sum some of those tiles for it.
+    import speculative_sampling_verify_03_amd as sv
+    k, B = 5, 160
+    rng = np.random.default_rng(5)
+    p = np.zeros((k + 1, V))
+    p[:, : V // 2] = rng.uniform(0.5, 1.5, size=(k + 1, V // 2))
+    p /= p.sum(axis=1, keepdims=True)
+    q = np.zeros((k, V))
+    q[:, V // 2:] = rng.uniform(0.5, 1.5, size=(k, V - V // 2))
+    q /= q.sum(axis=1, keepdims=True)
+    case = fixed_pq_case(p, q, B, seed=6, dtype=lt)
+    case.draft_probs = case.draft_probs.to(torch.bfloat16 if qt == "bf16" else torch.float32)
+    what = f"helped residual {lt}/{qt} V={V}"
+    announce(what)
+    ws = sv.new_workspace(sv.SV_KIND_LINEAR, B, k, V)
+    for rep in range(2):  # the second call finds the help words cleared by the first
+        got = run_linear(case.logits, case.draft_probs, case.draft_tokens, 1.0, 9, rep, ws=ws)
+        assert status_word(ws) == 0, f"{what}: a wait between workgroups ran out"
+        assert sections_clear(ws, sv.SV_KIND_LINEAR, k, V)
+        ref = oracle_linear(case.logits, case.draft_probs, case.draft_tokens, 1.0, 9, rep)
+        check_linear(got, ref, case.logits.dtype, X=case.draft_tokens.numpy(), V=V, what=f"{what} call {rep}")
+        assert np.all(got["accept_len"] == 0) and np.all(got["tokens"][:, 0] < V // 2)
+
+
 def test_deterministic_and_workspace_reuse():
     import speculative_sampling_verify_03_amd as sv
     case = linear_case(64, 5, 32000, seed=21, dtype="bf16", noise_sigma=0.7)
