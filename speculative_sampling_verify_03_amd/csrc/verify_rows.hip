@@ -94,7 +94,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
   // linear rows of several waves draw their position's pair in uniform control flow (below)
   constexpr bool UNIFORM_RNG = !TREE && NT >= 256;
-  __shared__ int s_xtok[LOSSLESS ? 64 : 1];  // lossless: the children's valid tokens
+  __shared__ int s_xtok[LOSSLESS ? 64 : 1];     // lossless: the children's valid tokens
+  __shared__ float s_xsub[LOSSLESS ? 64 : 1];   // and their weights 2^((l - m) c)
   __shared__ int s_nx;
 
   const int tid = threadIdx.x;
@@ -268,7 +269,13 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       // the children's valid tokens leave this node's draw
       const bool vx = g_node >= 0 && g_valid;
       const uint64_t vm = __ballot(vx);
-      if (vx) s_xtok[__popcll(vm & ((1ull << lane) - 1ull))] = g_x;
+      if (vx) {
+        const int at = __popcll(vm & ((1ull << lane) - 1ull));
+        s_xtok[at] = g_x;
+        // its weight in the draw from p, taken out of its unit's pass-1 total below (a
+        // repeated token once)
+        s_xsub[at] = dup ? 0.f : fast_exp2((g_l - m) * c);
+      }
       if (lane == 0) {
         s_nx = __popcll(vm);
         s_flag = (child_acc == 0ull);
@@ -407,15 +414,6 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   auto slot_bits = [&](const uint32_t (&em)[kMaskWords], int i) -> uint32_t {
     return (em[(i * VE) / 32] >> ((i * VE) & 31)) & ((1u << VE) - 1u);
   };
-  // Lossless tree: does unit q (tile q / NW, wave q % NW) hold one of the children's tokens?
-  auto unit_has_child = [&](int q) -> bool {
-    bool any = false;
-    for (int ci = 0; ci < nx; ++ci) {
-      const int vc = (s_xtok[ci] + h) / VE;
-      any = any || (vc / TILE) * NW + (vc % TILE) / (NV * kWave) == q;
-    }
-    return any;
-  };
   // candidate weights of one vector: 2^((l - m) c) for a bonus / tree draw, or the
   // residual max(0, p - q) at a rejected linear position (edge padding is -inf: 0), or
   // for the lossless tree 2^((l - m) c) with the children's tokens at 0 (`xb`: the mask
@@ -504,14 +502,24 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       bool clamp = false;
       int tile_s = 0, wave_s = 0;
       const int first = loaded_tile;
-      // A masked draw (lossless tree) takes the pass-1 partials for every unit except the
-      // few that hold a child's token; their owning waves recompute them with the mask.
-      // s_tot < 0 marks a unit that was not recomputed.
+      // A masked draw (lossless tree) takes the pass-1 partials for every unit; a unit that
+      // holds children's tokens has their weights taken out of its total (one thread, the
+      // children in order, so the bits do not depend on timing; a total that rounding
+      // leaves below 0 is 0).  s_tot < 0 marks a unit left as it was.  The walk recomputes
+      // the winning unit with the tokens masked, which agrees with this to rounding.
       if (masked) {
         for (int q = tid; q < nunits; q += NT) s_tot[q] = -1.f;
         __syncthreads();
+        if (tid == 0) {
+          for (int ci = 0; ci < nx; ++ci) {
+            const int vc = (s_xtok[ci] + h) / VE;
+            const int q = (vc / TILE) * NW + (vc % TILE) / (NV * kWave);
+            const float base = s_tot[q] >= 0.f ? s_tot[q] : s_ps[q] * fast_exp2((s_pm[q] - m) * c);
+            s_tot[q] = fmaxf(0.f, base - s_xsub[ci]);
+          }
+        }
       }
-      int step0 = (resid || masked) ? 0 : P.ntiles;
+      int step0 = resid ? 0 : P.ntiles;
       if (HELP && resid && P.help_on) {
         // The residual's tiles are claimed one at a time from the row's counter, which the
         // rows that help claim from too: the tile in registers first (never claimed), then
@@ -564,7 +572,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
         if (step < P.ntiles) {
           tile = first + step;  // (first + step) mod ntiles, both below ntiles
           if (tile >= P.ntiles) tile -= P.ntiles;
-          active = resid || (masked && unit_has_child(tile * NW + wid));
+          active = resid;
         } else {
           // a single-tile rejected row's deferred check: an earlier rejection posted
           // meanwhile makes this draw irrelevant
