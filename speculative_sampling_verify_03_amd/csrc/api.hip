@@ -106,6 +106,9 @@ int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* p
     std::memcpy(td.depth, ti->depth, 64);
     td.N = ti->N;
     td.D = ti->D;
+    P.tree_skip = 1;
+    for (int u = 0; u < ti->N; ++u)
+      if (ti->nchild[u] > 31) P.tree_skip = 0;
   }
   // How the residual reads q rows (see launch_rows): every logits row must have the same
   // 16-byte phase (whole-vector pitch), and the matching q chunks must line up with it.

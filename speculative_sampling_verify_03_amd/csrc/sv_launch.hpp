@@ -29,7 +29,12 @@ struct RowParams {
   uint64_t* seqword;       // [B][2] linear: inverted (row, token) key of the earliest
                            //     candidate, and 64 - row of the earliest rejection seen;
                            //     tree: mask of accepted nodes (word 0)
-  uint64_t* rowword;       // [B * R] tree: candidate token + 1 of each node
+  uint64_t* rowword;       // [B * R] tree: candidate token + 1 of each node (low half);
+                           //     with tree_skip, bit 63 once the node has decided its
+                           //     children and the kept ones above bit 32 (relative to its
+                           //     first child)
+  int32_t tree_skip;       // tree: nodes off every accepted path skip their draw (every
+                           //     node has at most 31 children)
   // Linear multi-tile rows (help_on): the rows after a sequence's earliest rejection
   // compute residual tiles of that rejected row (verify_rows.hip).
   uint64_t* help_words;    // per row help_stride words: (m, Z), tile claims, unit totals

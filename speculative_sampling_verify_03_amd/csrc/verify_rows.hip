@@ -243,6 +243,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   }
   uint64_t child_acc = 0;  // tree: this node's accepted children, as node bits (wave 0)
   uint64_t rej_dep = 0;    // linear: value returned by the rejection publish (waited on later)
+  uint64_t dec_dep = 0;    // tree: value returned by the early publish of the decisions
   if (LOSSLESS) {
     if (wid == 0) {
       // Sibling i (lane i) is tested against W_i = 1 - (mass of the distinct valid tokens
@@ -343,6 +344,49 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       }
     }
     s_flag = cand;
+  }
+  if (TREE && P.tree_skip && wid == 0) {
+    // A node publishes its children's decisions at once (bit 63 of its row word, the kept
+    // children above bit 32, relative to its first child; its drawn token joins the low
+    // half later).  A node that would draw first reads every node's word: the token is
+    // emitted only from the deepest node on an accepted path (the leftmost of the
+    // deepest), so the draw is skipped when a decided parent on its own path dropped it,
+    // or when some node whose whole path is decided and kept lies deeper, or as deep and
+    // further left.  Only decided parents count, so skipping changes no result.
+    if (lane == 0 && s_nc[j] > 0)
+      dec_dep = atomic_or_u64(&P.rowword[r], (1ull << 63) | ((child_acc >> s_fc[j]) << 32));
+    if (child_acc == 0ull && j > 0) {
+      const int N = P.R;
+      uint64_t w = 0;
+      if (lane < N)
+        w = __hip_atomic_load(P.rowword + static_cast<size_t>(b) * N + lane, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      const bool decided = lane < N && (w >> 63) != 0;
+      uint64_t kept = 0;  // this lane's node's kept children, as node bits
+      if (decided) kept = ((w >> 32) & ((1ull << s_nc[lane]) - 1ull)) << s_fc[lane];
+      const uint64_t dmask = __ballot(decided);
+      uint32_t klo = static_cast<uint32_t>(kept), khi = static_cast<uint32_t>(kept >> 32);
+      for (int o = 32; o >= 1; o >>= 1) {
+        klo |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(klo), o));
+        khi |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(khi), o));
+      }
+      const uint64_t amask = (static_cast<uint64_t>(khi) << 32) | klo;
+      // lane l's node: `sure` when every parent on its path decided and kept it, `off`
+      // when one of them decided and dropped it
+      bool sure = lane < N, off = false;
+      for (int x = lane; lane < N && x != 0; x = s_par[x]) {
+        const int px = s_par[x];
+        if (((dmask >> px) & 1ull) == 0) sure = false;
+        else if (((amask >> x) & 1ull) == 0) {
+          off = true;
+          sure = false;
+        }
+      }
+      const int dj = s_dep[j];
+      const bool ahead = sure && (s_dep[lane] > dj || (s_dep[lane] == dj && lane < j));
+      const bool self_off = __shfl(static_cast<int>(off), j) != 0;
+      if ((self_off || __ballot(ahead) != 0ull) && lane == 0) s_flag = 0;
+    }
   }
   if (tid == 0) {
     float us = g_usmp;  // linear: the pair of position j (drawn above for rows j < k)
@@ -877,8 +921,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   if (tid == 0) {
     uint64_t dep = 0;
     if (TREE) {
+      dep ^= dec_dep;
       if (child_acc) dep ^= atomic_or_u64(&P.seqword[2 * b], child_acc);
-      if (s_flag) dep ^= atomic_xchg_u64(&P.rowword[r], static_cast<uint64_t>(static_cast<uint32_t>(s_y + 1)));
+      if (s_flag) dep ^= atomic_or_u64(&P.rowword[r], static_cast<uint64_t>(static_cast<uint32_t>(s_y + 1)));
     } else {
       dep ^= rej_dep;
       if (s_flag) {
