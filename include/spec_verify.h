@@ -193,8 +193,14 @@ SV_API int spec_verify_tree_lossless(const void* target_logits, int lt, const in
  *   logits_out [B, k+1, V] f32    REQUIRED: receives hidden @ lm_head (fp32 accumulation);
  *                                 linear verification then runs on it.
  *   Other arguments as in spec_verify_linear.  H must be a multiple of 64 and `hidden`
- *   16-byte aligned; V is arbitrary (16-byte aligned lm_head rows, i.e. V % 8 == 0 and an
- *   aligned base, take the fast load path).  logits_out is overwritten on every call.
+ *   16-byte aligned; V is arbitrary.  With 16-byte aligned lm_head rows and logits_out
+ *   (V % 8 == 0 and aligned bases) and 16-byte aligned draft_probs, the GEMM also leaves
+ *   each row's softmax partials per block of 512 columns in the workspace and
+ *   verification starts from them (no second pass over the logits); other shapes verify
+ *   the written logits as spec_verify_linear does.  Results are the same either way.
+ *   logits_out is overwritten on every call.  Workspace: spec_verify_workspace_bytes
+ *   (SV_KIND_LMHEAD, B, k, V, H); its partials section is rewritten by every call, the
+ *   rest is returned to zero.
  */
 SV_API int spec_lmhead_verify(const void* hidden, const void* lm_head,
                        const void* draft_probs, int qt, const int32_t* draft_tokens,
@@ -203,6 +209,22 @@ SV_API int spec_lmhead_verify(const void* hidden, const void* lm_head,
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_target_prob, float* out_accept_prob,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The LM-head projection alone, the first stage of spec_lmhead_verify ("Accelerating
+ * Sonar through speculation", sections "EAGLE" and "Training MTP heads"): logits_out =
+ * hidden @ lm_head with fp32 accumulation, the same kernels and the same bits as the
+ * logits spec_lmhead_verify writes.  For callers that verify the logits themselves (for
+ * example greedily, with spec_verify_greedy).
+ *
+ *   hidden     [M, H] bf16   16-byte aligned; H a multiple of 64
+ *   lm_head    [H, V] bf16   row-major (vocabulary contiguous)
+ *   logits_out [M, V] f32    overwritten
+ * M = 0 does nothing.  Errors: SV_E_NULL, SV_E_SHAPE, SV_E_ALIGN, SV_E_DEVICE, SV_E_LAUNCH.
+ * No workspace.
+ */
+SV_API int spec_lmhead_logits(const void* hidden, const void* lm_head, int32_t M, int32_t H, int32_t V,
+                       float* logits_out, void* stream);
 
 /*
  * On-device token plug ("Accelerating Sonar through speculation", section "MTP schedule for

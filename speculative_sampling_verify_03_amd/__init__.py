@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     SpecVerifyError,
     library,
     new_workspace,
+    spec_lmhead_logits,
     spec_lmhead_verify,
     spec_verify_linear_noalloc,
     spec_lookup_drafts,

@@ -25,7 +25,7 @@ ERRORS = {
     -10: "SV_E_SCRATCH",
 }
 EXPORTS = ("spec_verify_linear", "spec_verify_linear_noalloc", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
-           "spec_lmhead_verify",
+           "spec_lmhead_verify", "spec_lmhead_logits",
            "spec_plug_tokens", "spec_lookup_drafts", "spec_verify_workspace_bytes", "spec_verify_strerror")
 
 
@@ -61,10 +61,11 @@ def _lib():
                                                   _U64, _U64, _P, _P, _P, _P, _SZ, _P]
         lib.spec_lmhead_verify.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _F32,
                                            _U64, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        lib.spec_lmhead_logits.argtypes = [_P, _P, _I32, _I32, _I32, _P, _P]
         lib.spec_plug_tokens.argtypes = [_P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P]
         lib.spec_lookup_drafts.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
         for fn in ("spec_verify_linear", "spec_verify_linear_noalloc", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_lossless",
-                   "spec_lmhead_verify",
+                   "spec_lmhead_verify", "spec_lmhead_logits",
                    "spec_plug_tokens", "spec_lookup_drafts"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.spec_verify_workspace_bytes.argtypes = [ctypes.c_int, _I32, _I32, _I32, _I32]
@@ -281,3 +282,18 @@ def spec_lmhead_verify(hidden, lm_head, draft_probs, draft_tokens, temperature, 
         _f32(out_accept_prob, (B, k), "out_accept_prob"),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(rc, "spec_lmhead_verify")
+
+
+def spec_lmhead_logits(hidden, lm_head, logits_out, stream=None):
+    """hidden bf16 [..., H] (M rows); lm_head bf16 [H, V]; logits_out float32 [..., V] with the
+    same leading shape: logits_out = hidden @ lm_head (the first stage of spec_lmhead_verify)."""
+    H = hidden.shape[-1]
+    V = lm_head.shape[1]
+    M = hidden.numel() // H if H else 0
+    if hidden.dtype != torch.bfloat16 or lm_head.dtype != torch.bfloat16 or lm_head.shape[0] != H:
+        raise ValueError("hidden [..., H] and lm_head [H, V] must be bfloat16")
+    if not hidden.is_contiguous() or not lm_head.is_contiguous():
+        raise ValueError("hidden and lm_head must be contiguous")
+    rc = _lib().spec_lmhead_logits(_ptr(hidden), _ptr(lm_head), M, H, V,
+                                   _f32(logits_out, tuple(hidden.shape[:-1]) + (V,), "logits_out"), _stream(stream))
+    _check(rc, "spec_lmhead_logits")

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["api.hip", "verify_rows.hip", "verify_split.hip", "verify_greedy.hip", "lmhead_gemm.hip", "plug.hip",
+HIP_SOURCES = ["api.hip", "verify_rows.hip", "verify_split.hip", "verify_greedy.hip", "lmhead_gemm.hip", "lmhead_verify.hip", "plug.hip",
                "lookup.hip"]
 CXX_SOURCES = ["validate.cpp"]
 

@@ -262,11 +262,58 @@ int spec_lmhead_verify(const void* hidden, const void* lm_head, const void* draf
   if ((rc = check_device())) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (sv::launch_lmhead_gemm(hidden, lm_head, logits_out, B * (k + 1), H, V, st) != hipSuccess)
+  // The direct GEMM kernel also writes each row's softmax partials per block of 512 columns;
+  // verification then starts from them instead of re-reading the float32 logits.  Other
+  // shapes and alignments verify the written logits with the row kernels.
+  const bool fused = sv::lmhead_gemm_direct(lm_head, logits_out, V) && sv::lmh_blocks(V) <= sv::kLmhMaxBlocks &&
+                     (k == 0 || (reinterpret_cast<uintptr_t>(draft_probs) & 15) == 0);
+  sv::WsLayout L;
+  sv::workspace_layout(SV_KIND_LMHEAD, B, k, V, H, &L);
+  char* w = static_cast<char*>(workspace);
+  const float c = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  uint64_t* part = fused ? reinterpret_cast<uint64_t*>(w + L.lmh_part_off) : nullptr;
+  if (sv::launch_lmhead_gemm(hidden, lm_head, logits_out, B * (k + 1), H, V, st, part, c) != hipSuccess)
     return SV_E_LAUNCH;
-  return run_rows(false, false, logits_out, SV_F32, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature, seed,
-                  offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr, nullptr,
-                  workspace, st);
+  if (!fused)
+    return run_rows(false, false, logits_out, SV_F32, draft_probs, qt, draft_tokens, B, k + 1, k, V, temperature,
+                    seed, offset, out_tokens, out_accept_len, out_target_prob, out_accept_prob, nullptr, nullptr,
+                    workspace, st);
+  sv::LmhParams P{};
+  P.logits = logits_out;
+  P.probs = draft_probs;
+  P.tokens = draft_tokens;
+  P.B = B;
+  P.R = k + 1;
+  P.k = k;
+  P.V = V;
+  P.nb = static_cast<int32_t>(sv::lmh_blocks(V));
+  P.nchunks = static_cast<int32_t>((static_cast<int64_t>(V) + 8191) / 8192);
+  P.cstride = static_cast<int32_t>(sv::lmh_chunks(V));
+  P.q_bf16 = (qt == SV_BF16);
+  P.c = c;
+  P.T = static_cast<double>(temperature);
+  P.seed = seed;
+  P.offset = offset;
+  P.out_tokens = out_tokens;
+  P.out_accept_len = out_accept_len;
+  P.out_tprob = out_target_prob;
+  P.out_aprob = out_accept_prob;
+  P.part = part;
+  P.seqw = reinterpret_cast<uint64_t*>(w + L.lmh_seq_off);
+  P.cmass = reinterpret_cast<uint32_t*>(w + L.lmh_mass_off);
+  P.ccnt = reinterpret_cast<uint32_t*>(w + L.lmh_cnt_off);
+  return sv::launch_lmhead_verify(P, st) == hipSuccess ? SV_OK : SV_E_LAUNCH;
+}
+
+int spec_lmhead_logits(const void* hidden, const void* lm_head, int32_t M, int32_t H, int32_t V, float* logits_out,
+                       void* stream) {
+  int rc = sv::validate_lmhead_logits(hidden, lm_head, M, H, V, logits_out);
+  if (rc != SV_OK || M == 0) return rc;
+  if ((rc = check_device())) return rc;
+  (void)hipGetLastError();
+  return sv::launch_lmhead_gemm(hidden, lm_head, logits_out, M, H, V, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SV_OK
+             : SV_E_LAUNCH;
 }
 
 int spec_verify_linear_noalloc(const void* target_logits, int lt, const void* draft_probs, int qt,

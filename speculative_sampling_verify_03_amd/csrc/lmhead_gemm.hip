@@ -276,7 +276,7 @@ __device__ __forceinline__ void copy16_to_lds(const SV_GLOBAL void* src, uint8_t
 template <int MB>
 __global__ __launch_bounds__(kDmaThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 lmhead_gemm_dma_kernel(const uint16_t* __restrict__ A_, const uint16_t* __restrict__ W_, float* __restrict__ C,
-                       int M, int H, int V) {
+                       int M, int H, int V, uint64_t* __restrict__ part, float c) {
   using S = DmaShape<MB>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -389,6 +389,52 @@ lmhead_gemm_dma_kernel(const uint16_t* __restrict__ A_, const uint16_t* __restri
   // no copy may still be writing this workgroup's LDS when it exits
   wait_vmcnt<0>();
 
+  if (part != nullptr) {
+    // Softmax partials of the verification that follows: per row, the (max, sum of
+    // 2^((l - max) c)) pair of this workgroup's 512 columns, from the accumulators as they
+    // are stored.  The 16 lanes of a k group (one DPP row) hold a row's 64 columns of this
+    // wave: its maximum by DPP max steps (lane 15 of the row), broadcast along the row by
+    // one more DPP move, then four exponentials per lane and DPP sums; the eight waves'
+    // pairs are merged in wave order through LDS.
+    lds_barrier();  // every wave has read its last stage: the ring's LDS is free
+    float2* sp = reinterpret_cast<float2*>(smem);  // [wave][16 * MB rows]
+    const bool col_ok = n_lane < V;                // four whole columns (V % 8 == 0)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = -INFINITY;
+        if (col_ok) x = fmaxf(fmaxf(acc[mb][0][i], acc[mb][1][i]), fmaxf(acc[mb][2][i], acc[mb][3][i]));
+        x = fmaxf(x, dpp_f<kDppShr1>(-INFINITY, x));
+        x = fmaxf(x, dpp_f<kDppShr2>(-INFINITY, x));
+        x = fmaxf(x, dpp_f<kDppShr4>(-INFINITY, x));
+        x = fmaxf(x, dpp_f<kDppShr8>(-INFINITY, x));
+        const float pm = dpp_f<kDppRowBcast15>(0.f, x);  // lane 15 of the row, to the whole row
+        const float pmc = pm * c;
+        float ps = 0.f;
+        if (col_ok) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ps += fast_exp2(fmaf(acc[mb][j][i], c, -pmc));
+        }
+        ps += dpp_f<kDppShr1>(0.f, ps);
+        ps += dpp_f<kDppShr2>(0.f, ps);
+        ps += dpp_f<kDppShr4>(0.f, ps);
+        ps += dpp_f<kDppShr8>(0.f, ps);
+        if ((lane & 15) == 15) sp[wid * (16 * MB) + mb * 16 + kg * 4 + i] = make_float2(pm, ps);
+      }
+    lds_barrier();
+    for (int t = tid; t < 16 * MB; t += kDmaThreads) {
+      if (m0 + t >= M) break;
+      float pm = -INFINITY, ps = 0.f;
+      for (int w = 0; w < kDmaWaves; ++w) {
+        const float2 q = sp[w * (16 * MB) + t];
+        merge_max_sum(pm, ps, q.x, q.y, c);
+      }
+      part[static_cast<size_t>(m0 + t) * gridDim.x + blockIdx.x] =
+          (static_cast<uint64_t>(__float_as_uint(pm)) << 32) | __float_as_uint(ps);
+    }
+  }
+
   if (n_lane >= V) return;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -403,7 +449,7 @@ lmhead_gemm_dma_kernel(const uint16_t* __restrict__ A_, const uint16_t* __restri
 
 template <int MB>
 static hipError_t launch_dma(const uint16_t* A, const uint16_t* W, float* C, int M, int H, int V, int gy,
-                             hipStream_t st) {
+                             uint64_t* part, float c, hipStream_t st) {
   static bool attr_set[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
@@ -414,7 +460,7 @@ static hipError_t launch_dma(const uint16_t* A, const uint16_t* W, float* C, int
     attr_set[dev] = true;
   }
   hipLaunchKernelGGL(lmhead_gemm_dma_kernel<MB>, dim3((V + kDmaBN - 1) / kDmaBN, gy), dim3(kDmaThreads),
-                     DmaShape<MB>::kLdsBytes, st, A, W, C, M, H, V);
+                     DmaShape<MB>::kLdsBytes, st, A, W, C, M, H, V, part, c);
   return hipGetLastError();
 }
 
@@ -432,18 +478,23 @@ static void launch_mb(const uint16_t* A, const uint16_t* W, float* C, int M, int
   }
 }
 
+bool lmhead_gemm_direct(const void* w, const float* logits, int V) {
+  // 16-byte copies of W need 16-byte aligned rows; 16-byte logits stores need 16-byte rows
+  return V % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+}
+
 hipError_t launch_lmhead_gemm(const void* hidden, const void* w, float* logits, int M, int H, int V,
-                              hipStream_t st) {
+                              hipStream_t st, uint64_t* part, float c) {
   const auto* A = static_cast<const uint16_t*>(hidden);
   const auto* Wp = static_cast<const uint16_t*>(w);
   const uintptr_t wa = reinterpret_cast<uintptr_t>(w), ca = reinterpret_cast<uintptr_t>(logits);
-  // 16-byte copies of W need 16-byte aligned rows; 16-byte logits stores need 16-byte rows
-  if (V % 8 == 0 && (wa & 15) == 0 && (ca & 15) == 0) {
+  if (lmhead_gemm_direct(w, logits, V)) {
     const int mblocks = (M + 15) / 16;
-    if (mblocks <= 4) return launch_dma<4>(A, Wp, logits, M, H, V, 1, st);
-    if (mblocks <= 8) return launch_dma<8>(A, Wp, logits, M, H, V, 1, st);
-    return launch_dma<12>(A, Wp, logits, M, H, V, (mblocks + 11) / 12, st);
+    if (mblocks <= 4) return launch_dma<4>(A, Wp, logits, M, H, V, 1, part, c, st);
+    if (mblocks <= 8) return launch_dma<8>(A, Wp, logits, M, H, V, 1, part, c, st);
+    return launch_dma<12>(A, Wp, logits, M, H, V, (mblocks + 11) / 12, part, c, st);
   }
+  if (part != nullptr) return hipErrorInvalidValue;  // partials come from the direct kernel only
   // 8-byte W loads need 8-byte aligned rows
   if (V % 4 == 0 && (wa & 7) == 0 && (ca & 15) == 0)
     launch_mb<true>(A, Wp, logits, M, H, V, st);

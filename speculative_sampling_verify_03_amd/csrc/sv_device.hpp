@@ -154,6 +154,7 @@ __device__ __forceinline__ int dpp_i(int identity, int x) {
 }
 constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
 constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+constexpr int kDppRowBcast15 = 0x15F;  // row_newbcast:15, lane 15 of each row of 16 to the row
 
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));

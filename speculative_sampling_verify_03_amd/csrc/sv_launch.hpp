@@ -119,9 +119,42 @@ constexpr int kGreedyFlatMaxGroups = 2048;   // eight 256-thread workgroups on e
 constexpr int kGreedyFlatMinVectors = 2048;  // at least one full batch per thread and a half
 hipError_t launch_greedy(const GreedyParams& P, bool bf16, hipStream_t st);
 
-// LM-head GEMM: logits[M, V] (fp32) = hidden[M, H] (bf16) @ W[H, V] (bf16).
+// LM-head GEMM: logits[M, V] (fp32) = hidden[M, H] (bf16) @ W[H, V] (bf16).  The direct
+// kernel (lmhead_gemm_direct: V % 8 == 0, W and logits 16-byte aligned) can also write, for
+// every row and block of kLmhBlockCols columns, the (max, sum of 2^((l - max) c)) pair of
+// those logits into part[M][ceil(V / kLmhBlockCols)] (high half max, low half sum, float32).
+constexpr int kLmhBlockCols = 512;
+bool lmhead_gemm_direct(const void* w, const float* logits, int V);
 hipError_t launch_lmhead_gemm(const void* hidden, const void* w, float* logits, int M, int H, int V,
-                              hipStream_t st);
+                              hipStream_t st, uint64_t* part = nullptr, float c = 0.f);
+
+// Verification of the LM head's logits from those partials (lmhead_verify.hip): a decide
+// kernel (one workgroup per sequence) and a draw kernel (one wave per block of columns of
+// each sequence's emitted row).
+struct LmhParams {
+  const float* logits;     // [B * R, V] float32, as the GEMM wrote them
+  const void* probs;       // [B, k, V], float32 or bfloat16, 16-byte aligned (k > 0)
+  const int32_t* tokens;   // [B, k]
+  int32_t B, R, k, V;
+  int32_t nb;              // column blocks per row = ceil(V / kLmhBlockCols)
+  int32_t nchunks;         // residual chunks per row = ceil(V / 8192)
+  int32_t cstride;         // chunk words per sequence in cmass (>= nchunks, <= 64)
+  int32_t q_bf16;
+  float c;                 // log2(e) / T
+  double T;
+  uint64_t seed, offset;
+  int32_t* out_tokens;
+  int32_t* out_accept_len;
+  float* out_tprob;
+  float* out_aprob;
+  const uint64_t* part;    // [B * R][nb] the GEMM's partials (rewritten by every call)
+  // zero on entry, returned to zero by the draw kernel:
+  uint64_t* seqw;          // [B][2] emitted position n + 1, and row n's (max, sum)
+  uint32_t* cmass;         // [B][cstride] residual mass of each chunk of row n
+  uint32_t* ccnt;          // [B] column blocks counted
+};
+constexpr int kLmhMaxBlocks = 1024;  // nb limit of the draw kernel's block pick
+hipError_t launch_lmhead_verify(const LmhParams& P, hipStream_t st);
 
 // Token plug: one wave per sequence.
 struct PlugParams {

@@ -64,7 +64,14 @@ bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H,
   out->help_off = out->row_off + round_up(rows * w);
   const bool linear = kind == SV_KIND_LINEAR || kind == SV_KIND_LMHEAD;
   const size_t hrows = linear ? (rows < static_cast<size_t>(kHelpRows) ? rows : static_cast<size_t>(kHelpRows)) : 0;
-  out->total = out->help_off + round_up(hrows * static_cast<size_t>(help_stride(V)) * w);
+  out->lmh_part_off = out->help_off + round_up(hrows * static_cast<size_t>(help_stride(V)) * w);
+  const bool lmh = kind == SV_KIND_LMHEAD;
+  const size_t nb = lmh ? static_cast<size_t>(lmh_blocks(V)) : 0;
+  out->lmh_seq_off = out->lmh_part_off + round_up(rows * nb * w);
+  out->lmh_mass_off = out->lmh_seq_off + round_up((lmh ? 2 * b : 0) * w);
+  const size_t nch = lmh ? static_cast<size_t>(lmh_chunks(V)) : 0;
+  out->lmh_cnt_off = out->lmh_mass_off + round_up(b * nch * sizeof(uint32_t));
+  out->total = out->lmh_cnt_off + round_up((lmh ? b : 0) * sizeof(uint32_t));
   return true;
 }
 
@@ -192,6 +199,17 @@ int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt
   if ((reinterpret_cast<uintptr_t>(logits_out) & 3)) return SV_E_ALIGN;
   if (k > 0 && (rc = check_aligned(probs, qt))) return rc;
   return check_ws(ws, ws_bytes, SV_KIND_LMHEAD, B, k, V, H);
+}
+
+int validate_lmhead_logits(const void* hidden, const void* w, int32_t M, int32_t H, int32_t V,
+                           const float* logits_out) {
+  if (M < 0 || H < 1 || H % 64 != 0 || H > (1 << 20) || V < 1 || V > kMaxV) return SV_E_SHAPE;
+  if (!mul_ok(M, 1, kMaxTotalRows * kMaxRows)) return SV_E_SHAPE;
+  if (M == 0) return SV_OK;
+  if (!hidden || !w || !logits_out) return SV_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(w) & 1)) return SV_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(logits_out) & 3)) return SV_E_ALIGN;
+  return SV_OK;
 }
 
 int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, int32_t W, const int32_t* seq_len,

@@ -34,10 +34,21 @@ constexpr int kSplitWordsPerRow = 6 * kSplitSlices + 5;
 constexpr int64_t kHelpRows = 2048;
 inline int32_t help_stride(int32_t V) { return 2 + (V + 3) / 4096 + 9; }
 
+// The LM-head call adds, after the linear sections, the GEMM's softmax partials (one u64
+// per row and block of 512 columns, rewritten by every call), two hand-over words and a
+// chunk counter per sequence, and one residual mass per sequence and chunk of 8192 columns
+// (returned to zero by every call).
+inline int64_t lmh_blocks(int32_t V) { return (static_cast<int64_t>(V) + 511) / 512; }
+inline int64_t lmh_chunks(int32_t V) {
+  const int64_t c = (static_cast<int64_t>(V) + 8191) / 8192;
+  return c < 64 ? c : 64;
+}
+
 struct WsLayout {
   size_t status_off, gen_off, rej_off, words_off;  // fixed prefix
   size_t counters_off, seq_off, row_off;           // row kernel, greedy and tree kernels
   size_t help_off;                                 // row kernel, linear (0 size otherwise)
+  size_t lmh_part_off, lmh_seq_off, lmh_mass_off, lmh_cnt_off;  // LM-head (0 size otherwise)
   size_t total;
 };
 bool workspace_layout(int kind, int32_t B, int32_t k_or_N, int32_t V, int32_t H, WsLayout* out);
@@ -76,6 +87,9 @@ int validate_tree_lossless(const void* logits, int lt, const int32_t* node_token
 int validate_lmhead(const void* hidden, const void* w, const void* probs, int qt, const int32_t* tokens,
                     int32_t B, int32_t k, int32_t H, int32_t V, float T, const float* logits_out,
                     const int32_t* out_tokens, const int32_t* out_len, const void* ws, size_t ws_bytes);
+
+int validate_lmhead_logits(const void* hidden, const void* w, int32_t M, int32_t H, int32_t V,
+                           const float* logits_out);
 
 int validate_plug(const int32_t* tokens, const int32_t* accept_len, int32_t B, int32_t W, const int32_t* seq_len,
                   const int32_t* history, int32_t cap, const int32_t* next_token, const int32_t* status);

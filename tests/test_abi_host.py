@@ -177,6 +177,23 @@ def test_lmhead_validation_codes():
     assert lmhead(B=0) == 0
 
 
+def lmhead_logits(**kw):
+    a = dict(h=C(0x1000), w=FAKE, M=12, H=128, V=100, logits=FAKE, stream=None)
+    a.update(kw)
+    return sv.library().spec_lmhead_logits(*a.values())
+
+
+def test_lmhead_logits_validation_codes():
+    assert lmhead_logits(M=0) == 0
+    assert lmhead_logits(logits=None) == -1
+    assert lmhead_logits(w=None) == -1
+    assert lmhead_logits(H=96) == -2        # H must be a multiple of 64
+    assert lmhead_logits(M=-1) == -2
+    assert lmhead_logits(V=0) == -2
+    assert lmhead_logits(h=C(0x1008)) == -9  # hidden must be 16-byte aligned
+    assert lmhead_logits(logits=C(0x1002)) == -9
+
+
 def plug(**kw):
     a = dict(toks=FAKE, alen=FAKE, B=2, W=6, seq=FAKE, hist=FAKE, cap=100, nxt=None, status=None, stream=None)
     a.update(kw)

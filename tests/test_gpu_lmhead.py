@@ -142,3 +142,66 @@ def test_lmhead_cfg4_full():
     exact = check_gemm(got["logits"], case, what)
     check_verify_on_gpu_logits(got, case, 0, what=what)
     check_verify_from_inputs(got, case, exact, 0, what=what)
+
+
+# The direct kernel (V % 8 == 0, aligned W and logits) also writes per-block softmax
+# partials, and verification then runs from them (decide, then a chunked draw); the cases
+# below pin that path at its edges.
+@pytest.mark.parametrize("B,k,H,V,T,qt", [(24, 4, 128, 20000, 0.7, torch.bfloat16),
+                                          (9, 7, 64, 33000, 1.5, torch.float32),
+                                          (64, 1, 64, 8200, 1.0, torch.bfloat16)])
+def test_lmhead_fused_shapes(B, k, H, V, T, qt):
+    case = lmhead_case(B, k, H, V, seed=B + V, temperature=T)
+    case.draft_probs = case.draft_probs.to(qt)
+    what = f"lmhead fused B={B} k={k} H={H} V={V} T={T} q={qt}"
+    announce(what)
+    got = run_lmhead(case, seed=7, offset=3)
+    exact = check_gemm(got["logits"], case, what)
+    check_verify_on_gpu_logits(got, case, 7, offset=3, what=what)
+    check_verify_from_inputs(got, case, exact, 7, offset=3, what=what)
+
+
+def test_lmhead_fused_invalid_tokens():
+    # out-of-range draft tokens are rejected (p(x) = 0), so those sequences draw their
+    # residual at that position
+    B, k, H, V = 16, 3, 64, 4096
+    case = lmhead_case(B, k, H, V, seed=5)
+    case.draft_tokens[:, 1] = torch.tensor([-1, V, 10**6, -(10**6)] * 4, dtype=torch.int32)
+    got = run_lmhead(case, seed=2)
+    check_verify_on_gpu_logits(got, case, 2, what="lmhead fused invalid tokens")
+    assert np.all(got["accept_len"] <= 1)
+
+
+def test_lmhead_fused_empty_residual():
+    # hidden = e_0, W row 0 = 1000 at one column and 0 elsewhere: every row's p is one-hot
+    # (the other terms, e^-1000, underflow to zero in float32 and in float64 alike), q is the
+    # same one-hot and the draft token is another column (q(x) = p(x) = 0): rejected,
+    # max(0, p - q) = 0 everywhere, and the token is drawn from p itself: the hot column
+    B, k, H, V, hot = 8, 2, 64, 2048, 1234
+    hidden = torch.zeros((B, k + 1, H), dtype=torch.bfloat16)
+    hidden[:, :, 0] = 1.0
+    w = torch.zeros((H, V), dtype=torch.bfloat16)
+    w[0, hot] = 1000.0
+    q = torch.zeros((B, k, V), dtype=torch.float32)
+    q[:, :, hot] = 1.0
+    from synthetic.generators import LMHeadCase
+    case = LMHeadCase(hidden=hidden, weight=w, draft_probs=q,
+                      draft_tokens=torch.full((B, k), 7, dtype=torch.int32), temperature=1.0, meta={})
+    got = run_lmhead(case, seed=1)
+    check_verify_on_gpu_logits(got, case, 1, what="lmhead fused empty residual")
+    assert np.all(got["accept_len"] == 0) and np.all(got["tokens"][:, 0] == hot)
+
+
+@pytest.mark.parametrize("B,k,H,V", [(4, 3, 128, 1000), (16, 5, 256, 4096), (32, 5, 8192, 128256)])
+def test_lmhead_logits_alone(B, k, H, V):
+    # spec_lmhead_logits: the same kernels (and bits) as the logits spec_lmhead_verify writes
+    case = cfg4_case() if V == 128256 else lmhead_case(B, k, H, V, seed=B * 7 + V)
+    what = f"lmhead logits alone M={B * (k + 1)} H={H} V={V}"
+    announce(what)
+    got = run_lmhead(case, seed=3)
+    alone = torch.full((B, k + 1, V), float("nan"), dtype=torch.float32, device=DEV)
+    sv.spec_lmhead_logits(case.hidden.to(DEV), case.weight.to(DEV), alone)
+    torch.cuda.synchronize()
+    assert torch.equal(alone.cpu(), got["logits"]), f"{what}: logits differ from the verify call's"
+    if V != 128256:
+        check_gemm(alone.cpu(), case, what)
