@@ -166,6 +166,22 @@ void lmhead() {
   EXPECT(validate_lmhead(P, P, P, SV_BF16, I, 4, 3, 128, 100, 1.f, reinterpret_cast<const float*>(0x3002), I, I,
                          WS, BIG), SV_E_ALIGN);
   EXPECT(validate_lmhead(P, P, P, SV_BF16, I, 4, 3, 128, 100, 1.f, F, I, I, WS, 1), SV_E_WORKSPACE);
+
+  using sv::validate_lmhead_logits;
+  EXPECT(validate_lmhead_logits(P, P, 24, 128, 100, F), SV_OK);
+  EXPECT(validate_lmhead_logits(nullptr, nullptr, 0, 128, 100, nullptr), SV_OK);
+  EXPECT(validate_lmhead_logits(nullptr, P, 24, 128, 100, F), SV_E_NULL);
+  EXPECT(validate_lmhead_logits(P, nullptr, 24, 128, 100, F), SV_E_NULL);
+  EXPECT(validate_lmhead_logits(P, P, 24, 128, 100, nullptr), SV_E_NULL);
+  EXPECT(validate_lmhead_logits(P, P, -1, 128, 100, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(P, P, INT32_MAX, 128, 100, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(P, P, 24, 96, 100, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(P, P, 24, INT32_MIN, 100, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(P, P, 24, 128, 0, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(P, P, 24, 128, INT32_MAX, F), SV_E_SHAPE);
+  EXPECT(validate_lmhead_logits(reinterpret_cast<const void*>(0x1008), P, 24, 128, 100, F), SV_E_ALIGN);
+  EXPECT(validate_lmhead_logits(P, reinterpret_cast<const void*>(0x1001), 24, 128, 100, F), SV_E_ALIGN);
+  EXPECT(validate_lmhead_logits(P, P, 24, 128, 100, reinterpret_cast<const float*>(0x3002)), SV_E_ALIGN);
 }
 
 void plug_lookup() {
@@ -229,6 +245,19 @@ void workspace() {
   if (A.status_off != Bl.status_off || A.gen_off != Bl.gen_off || A.rej_off != Bl.rej_off ||
       A.words_off != Bl.words_off || A.counters_off != Bl.counters_off || A.counters_off <= A.words_off) {
     std::printf("FAIL the workspace prefix moved between layouts\n");
+    ++failures;
+  }
+  // the LM-head kind adds its sections after the linear ones: partials per row and 512-column
+  // block, two words per sequence, one mass per sequence and 8192-column chunk, a counter
+  sv::WsLayout Li, Lm;
+  EXPECT(sv::workspace_layout(SV_KIND_LINEAR, 32, 5, 128256, 8192, &Li), true);
+  EXPECT(sv::workspace_layout(SV_KIND_LMHEAD, 32, 5, 128256, 8192, &Lm), true);
+  ++checks;
+  if (Lm.lmh_part_off != Li.total || Lm.lmh_seq_off < Lm.lmh_part_off + size_t(192) * 251 * 8 ||
+      Lm.lmh_mass_off < Lm.lmh_seq_off + size_t(32) * 16 || Lm.lmh_cnt_off < Lm.lmh_mass_off + size_t(32) * 16 * 4 ||
+      Lm.total < Lm.lmh_cnt_off + size_t(32) * 4 || Lm.lmh_part_off % 256 || Lm.lmh_cnt_off % 256) {
+    std::printf("FAIL LM-head sections: part %zu seq %zu mass %zu cnt %zu total %zu (linear total %zu)\n",
+                Lm.lmh_part_off, Lm.lmh_seq_off, Lm.lmh_mass_off, Lm.lmh_cnt_off, Lm.total, Li.total);
     ++failures;
   }
   EXPECT(sv::workspace_layout(7, 1, 1, 1, 1, &L), false);
