@@ -92,6 +92,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   constexpr bool HELP = !TREE && NV == 16;
   // single-tile linear rows with q vectors in phase: the rejection check is deferred (below)
   constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
+  // single-tile rows: a draw from p is walked from the registers (below)
+  constexpr bool REG_DRAW = NV <= 8;
   // linear rows of several waves draw their position's pair in uniform control flow (below)
   constexpr bool UNIFORM_RNG = !TREE && NT >= 256;
   __shared__ int s_xtok[LOSSLESS ? 64 : 1];     // lossless: the children's valid tokens
@@ -668,10 +670,13 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           wave_s = star - tile_s * NW;
           tile = tile_s;
           // The winning unit's weights are recomputed by every wave together (a quarter or an
-          // eighth of its slots each; the unit is reloaded, from cache when it is the tile in
-          // registers) unless a residual draw already holds them in the winner's registers.
-          coop = !resid || tile_s != loaded_tile;
-          active = false;
+          // eighth of its slots each, the unit reloaded) unless a residual draw already holds
+          // them in the winner's registers.  Single-tile rows hold the whole row: a draw from
+          // p there is walked by the winner wave from its registers after this step sums its
+          // slots (B=1000 k=4 V=1024: 13.3 -> 12.8 us); a unit of a 16-vector tile is cheaper
+          // to split over the waves (every wave summing its own measured 0.5 us slower).
+          coop = REG_DRAW ? tile_s != loaded_tile : (!resid || tile_s != loaded_tile);
+          active = REG_DRAW && !coop && !resid && wid == wave_s;
         }
         if (active) {
           const int v0 = tile * TILE + wid * (NV * kWave) + lane;
