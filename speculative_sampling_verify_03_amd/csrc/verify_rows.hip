@@ -319,9 +319,17 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
           if (seen > static_cast<uint64_t>(64 - j)) cand = false;
         }
       } else if (cand) {  // the last row: any rejection makes it irrelevant
-        const uint64_t seen =
-            __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+        if (DEFER) {
+          // a single-tile row walks its draw from registers for less than the load's round
+          // trip: it draws anyway and reads the answer only when it would post the draw
+          int zero;
+          asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+          rej_dep = __hip_atomic_load(&P.seqword[2 * b + 1 + zero], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          const uint64_t seen =
+              __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (seen > static_cast<uint64_t>(64 - j)) cand = false;
+        }
       }
     }
     s_help = -1;
@@ -931,7 +939,10 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       if (s_flag) dep ^= atomic_or_u64(&P.rowword[r], static_cast<uint64_t>(static_cast<uint32_t>(s_y + 1)));
     } else {
       dep ^= rej_dep;
-      if (s_flag) {
+      // the last row's deferred check (single-tile rows): an earlier rejection makes its draw
+      // irrelevant, so it is not posted
+      const bool post = s_flag && !(DEFER && j == P.k && rej_dep > static_cast<uint64_t>(64 - j));
+      if (post) {
         const uint64_t key = (static_cast<uint64_t>(j) << 32) | static_cast<uint32_t>(s_y);
         dep ^= atomic_max_u64(&P.seqword[2 * b], ~key);
       }
