@@ -64,7 +64,9 @@ struct RowOccupancy<512, 8> {
   static constexpr int kWavesPerEU = 4;
 };
 
-template <bool BF16, int NT, int NV, bool TREE, int QMODE>
+// STOP: linear rows walked in 256 x 16 tiles stop streaming once an earlier position of
+// their sequence has rejected (an instance of its own, launched for grids of several rounds).
+template <bool BF16, int NT, int NV, bool TREE, int QMODE, bool STOP = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(QMODE == kQLossless ? 4 : RowOccupancy<NT, NV>::kWavesPerEU)))
 void row_verify_kernel(RowParams P, TreeDesc td) {
   using E = Elem<BF16>;
@@ -83,6 +85,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   __shared__ int s_flag, s_y, s_last, s_skip;
   __shared__ float s_slot[NV];    // a cooperatively recomputed unit's slot totals
   __shared__ int s_claim[2], s_hr, s_help;  // residual tiles claimed; the row this one helps
+  __shared__ int s_quit[NT / kWave];        // per wave: stopped streaming (below)
   __shared__ float s_hm, s_hz;                      // the helped row's (max, sum)
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
@@ -90,6 +93,9 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   // linear rows walked in tiles (16 vectors per thread: the single-tile shapes hold fewer)
   // can be helped by workgroups that are done (below)
   constexpr bool HELP = !TREE && NV == 16;
+  // linear rows walked in tiles stop streaming once an earlier position has rejected
+  // (below)
+  constexpr bool QUIT = STOP && !TREE && NV == 16 && NT < 512;
   // single-tile linear rows with q vectors in phase: the rejection check is deferred (below)
   constexpr bool DEFER = !TREE && QMODE == kQVec && NV <= 8;
   // single-tile rows: a draw from p is walked from the registers (below)
@@ -167,11 +173,26 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) dst[i] = ld16_stream(vrow, v0 + i * kWave, nvec);  // edges: mask_edges
   };
+  // A row after its sequence's earliest rejection supplies nothing to the outputs (the
+  // sequential rule stops there), except p_j(x_j) when that is asked for (rows j < k).
+  // Such a row reads the rejection word as each tile is issued and stops streaming once
+  // it shows a rejection before j; the word only grows while the sequence is running.
+  // Each wave decides for itself (the word may change between two waves' reads) and the
+  // row stops when any of them did.  (Rows that prefetch the next tile are few per batch
+  // and keep streaming.)
+  const bool may_quit = QUIT && j > 0 && (j == P.k || (P.out_tprob == nullptr && P.out_aprob == nullptr));
+  bool quit = false;
   if (PIPE) load_tile(buf, 0);
   for (int tile = 0; tile < P.ntiles; ++tile) {
     const int v0 = tile * TILE + wid * (NV * kWave) + lane;
     // every load of the tile is in flight before the first edge mask
     if (!PIPE) load_tile(buf, tile);
+    uint64_t chk = 0;
+    if (QUIT) {  // every row reads it (a branch around the load made the compiler wait for
+                 // it before the next tile's loads)
+      asm volatile("" ::: "memory");  // issued behind the tile's loads
+      chk = __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     else if (tile + 1 < P.ntiles) load_tile(nxt, tile + 1);
     // Linear rows of several waves: the pair of position j is the same for every thread,
     // so every thread draws it in uniform control flow (scalar instructions) while the
@@ -182,16 +203,40 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     // one-lane draw.
     if (UNIFORM_RNG && tile == 0)
       draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(j), g_uacc, g_usmp);
+    // The gathers of a single-tile row are issued right behind its loads, before the edge
+    // masks whose waits would hold them (and the one-lane uniform draw) until the whole
+    // tile has arrived (B=1000 k=4 V=1024: 12.7 -> 12.2 us); multi-tile rows measured
+    // nothing either way and keep them behind the masks.
+    if constexpr (NV <= 8) {
+      if (tile == 0 && g_node >= 0) {
+        g_valid = (g_x >= 0 && g_x < V);
+        if (g_valid) {
+          g_l = load_elem(rowp, g_x, BF16);
+          if (!LOSSLESS) g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
+        }
+        if (!UNIFORM_RNG)
+          draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) buf[i] = mask_edges<BF16>(buf[i], (v0 + i * kWave) * VE - h, V);
-    if (tile == 0 && g_node >= 0) {
-      g_valid = (g_x >= 0 && g_x < V);
-      if (g_valid) {
-        g_l = load_elem(rowp, g_x, BF16);
-        if (!LOSSLESS) g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
+    if constexpr (NV > 8) {
+      if (tile == 0 && g_node >= 0) {
+        g_valid = (g_x >= 0 && g_x < V);
+        if (g_valid) {
+          g_l = load_elem(rowp, g_x, BF16);
+          if (!LOSSLESS) g_q = load_elem(static_cast<const char*>(P.probs) + g_qrow * V * qeb, g_x, P.q_bf16);
+        }
+        if (!UNIFORM_RNG)
+          draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
       }
-      if (!UNIFORM_RNG)
-        draw_uniforms(P.seed, P.offset, static_cast<uint32_t>(b), static_cast<uint32_t>(g_node), g_uacc, g_usmp);
+    }
+    if (QUIT) {
+      asm volatile("" : "+v"(chk)::"memory");  // read here, once the tile has arrived
+      if (may_quit && chk > static_cast<uint64_t>(64 - j)) {
+        quit = true;
+        break;
+      }
     }
     float tm = -INFINITY;
 #pragma unroll
@@ -219,8 +264,15 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     }
   }
   pin_packed(buf);  // pass 2 starts again from the packed row
+  if (may_quit && lane == 0) s_quit[wid] = quit ? 1 : 0;
   __syncthreads();
-  // every thread merges the partials in the same order: the row's (m, Z)
+  bool row_quit = false;
+  if (may_quit) {
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) row_quit = row_quit || s_quit[w] != 0;
+  }
+  // every thread merges the partials in the same order: the row's (m, Z) (meaningless for
+  // a row that stopped, which uses neither)
   float m = -INFINITY, Z = 0.f;
   for (int q = 0; q < nunits; ++q) merge_max_sum(m, Z, s_pm[q], s_ps[q], c);
 
@@ -290,8 +342,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
       if (lane == 0) s_flag = (child_acc == 0ull);
     }
   } else if (tid == 0) {
-    const bool rejected = !acc && j < P.k;
-    bool cand = (j == P.k) || rejected;
+    const bool rejected = !acc && j < P.k && !row_quit;
+    bool cand = !row_quit && ((j == P.k) || rejected);
     // A rejected row publishes its rejection at once (the word holds 64 - row of the
     // earliest rejection seen) and consults it before its costly candidate pass: only the
     // earliest rejected row can supply the emitted token, and the earliest one never sees
@@ -1047,11 +1099,39 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
 }
 
 // ------------------------------------------------------------------ launch table
-template <bool BF16, int NT, int NV, bool TREE, int QMODE>
+template <bool BF16, int NT, int NV, bool TREE, int QMODE, bool STOP = false>
 static hipError_t launch_one(const RowParams& P, const TreeDesc& td, int grid, hipStream_t st) {
   const size_t lds = 3 * static_cast<size_t>(P.ntiles) * (NT / kWave) * sizeof(float);
-  hipLaunchKernelGGL((row_verify_kernel<BF16, NT, NV, TREE, QMODE>), dim3(grid), dim3(NT), lds, st, P, td);
+  hipLaunchKernelGGL((row_verify_kernel<BF16, NT, NV, TREE, QMODE, STOP>), dim3(grid), dim3(NT), lds, st, P, td);
   return hipGetLastError();
+}
+
+// Linear rows of 256 x 16 tiles stop streaming after an earlier rejection only when the
+// grid takes several rounds of workgroups: the rows of a later round then start after the
+// earlier positions have decided (B=256 k=8 V=128256: 134 -> 113 us).  In a single round
+// the per-tile reads of the rejection word cost more than they saved (B=256 k=1: 46.0 ->
+// 46.8 us), so that grid runs the instance without them.
+template <bool BF16, bool TREE, int QMODE>
+static hipError_t launch_tiles_256(const RowParams& P, const TreeDesc& td, int grid, hipStream_t st) {
+  if (TREE) return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
+  static int cap[64] = {};  // workgroups of the instance the device holds at once, per device
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    c = __atomic_load_n(&cap[dev], __ATOMIC_RELAXED);
+    if (c == 0) {
+      const size_t lds = 3 * static_cast<size_t>(P.ntiles) * (256 / kWave) * sizeof(float);
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, row_verify_kernel<BF16, 256, 16, TREE, QMODE, true>,
+                                                       256, lds) == hipSuccess &&
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
+          cus > 0) {
+        c = per_cu * cus;
+        __atomic_store_n(&cap[dev], c, __ATOMIC_RELAXED);
+      }
+    }
+  }
+  if (c > 0 && grid > c) return launch_one<BF16, 256, 16, TREE, QMODE, true>(P, td, grid, st);
+  return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
 }
 
 template <bool BF16, bool TREE, int QMODE>
@@ -1060,7 +1140,7 @@ static hipError_t launch_rows_t(const RowParams& P, const TreeDesc& td, int cfg,
     case 0: return launch_one<BF16, 64, 4, TREE, QMODE>(P, td, grid, st);
     case 1: return launch_one<BF16, 256, 4, TREE, QMODE>(P, td, grid, st);
     case 2: return launch_one<BF16, 512, 8, TREE, QMODE>(P, td, grid, st);
-    case 3: return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
+    case 3: return launch_tiles_256<BF16, TREE, QMODE>(P, td, grid, st);
     default: return launch_one<BF16, 512, 16, TREE, QMODE>(P, td, grid, st);
   }
 }

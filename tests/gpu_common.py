@@ -54,20 +54,25 @@ def on_device(t: torch.Tensor, misalign: int = 0) -> torch.Tensor:
     return out
 
 
-def run_linear(logits, probs, tokens, T, seed, offset=0, misalign=(0, 0), ws=None, stream=None):
+def run_linear(logits, probs, tokens, T, seed, offset=0, misalign=(0, 0), ws=None, stream=None, with_probs=True):
+    """with_probs=False asks for tokens and lengths only (no p_j(x_j) outputs), which lets
+    rows after a sequence's first rejection stop early; the probability arrays come back
+    empty."""
     B, R, V = logits.shape
     k = R - 1
     lg = on_device(logits, misalign[0])
     q = on_device(probs, misalign[1])
     x = tokens.to(DEV)
+    pk = k if with_probs else 0
     out = dict(tokens=torch.full((B, R), -7, dtype=torch.int32, device=DEV),
                accept_len=torch.full((B,), -7, dtype=torch.int32, device=DEV),
-               target_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV),
-               accept_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV))
+               target_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV)[:, :pk],
+               accept_prob=torch.full((B, k), -7.0, dtype=torch.float32, device=DEV)[:, :pk])
     if ws is None:
         ws = sv.new_workspace(sv.SV_KIND_LINEAR, B, k, V)
     sv.spec_verify_linear(lg, q, x, T, seed, offset, out["tokens"], out["accept_len"],
-                          out["target_prob"], out["accept_prob"], ws, stream)
+                          out["target_prob"] if with_probs else None, out["accept_prob"] if with_probs else None,
+                          ws, stream)
     torch.cuda.synchronize()
     return {n: t.cpu().numpy() for n, t in out.items()}
 

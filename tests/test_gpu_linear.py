@@ -12,11 +12,11 @@ from synthetic import cfg1_case, cfg2_case, cfg3_case, fixed_pq_case, linear_cas
 pytestmark = pytest.mark.gpu
 
 
-def _case_run(case, seed=0, offset=0, misalign=(0, 0), what=""):
+def _case_run(case, seed=0, offset=0, misalign=(0, 0), what="", with_probs=True):
     announce(f"{what}: B={case.B} k={case.k} V={case.V} {case.logits.dtype} T={case.temperature} "
-             f"misalign={misalign}")
+             f"misalign={misalign} probabilities={'on' if with_probs else 'off'}")
     got = run_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset,
-                     misalign)
+                     misalign, with_probs=with_probs)
     ref = oracle_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset)
     check_linear(got, ref, case.logits.dtype, X=case.draft_tokens.numpy(), V=case.V, what=what)
     return got, ref
@@ -67,6 +67,14 @@ def test_cfg3_full_stochastic():
 def test_mtp_single_token_regime():
     # one drafted token per sequence, 256 sequences, Llama-3 vocabulary
     _case_run(mtp_case(), seed=0, what="B=256 k=1 V=128256 bf16 (MTP regime)")
+
+
+@pytest.mark.parametrize("name,seed", [("cfg3", 1), ("mtp", 0), ("mtp", 1)])
+def test_tokens_only_full_size(name, seed):
+    # without p_j(x_j) outputs the rows after a sequence's first rejection stop streaming
+    # once they see it; tokens and lengths must not change
+    case = cfg3_case() if name == "cfg3" else mtp_case()
+    _case_run(case, seed=seed, what=f"{name} tokens only, seed {seed}", with_probs=False)
 
 
 @pytest.mark.parametrize("dtype,V", [("f32", 1003), ("bf16", 1001), ("f32", 5), ("bf16", 1), ("bf16", 777),

@@ -15,10 +15,11 @@ pytestmark = pytest.mark.gpu
 _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def _run(case, seed, what, ws=None, offset=0):
+def _run(case, seed, what, ws=None, offset=0, with_probs=True):
     announce(f"{what}: B={case.B} k={case.k} V={case.V} {case.logits.dtype}/{case.draft_probs.dtype} "
-             f"T={case.temperature} seed={seed}")
-    got = run_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset, ws=ws)
+             f"T={case.temperature} seed={seed} probabilities={'on' if with_probs else 'off'}")
+    got = run_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset, ws=ws,
+                     with_probs=with_probs)
     ref = oracle_linear(case.logits, case.draft_probs, case.draft_tokens, case.temperature, seed, offset)
     check_linear(got, ref, case.logits.dtype, X=case.draft_tokens.numpy(), V=case.V, what=what)
     return got, ref
@@ -50,6 +51,20 @@ def test_long_rows_single_draft_many_rows():
 def test_long_rows_long_draft():
     case = linear_case(6, 40, 70000, seed=7, dtype="f32", noise_sigma=0.3)
     _run(case, 5, "long rows k=40")
+
+
+@pytest.mark.parametrize("B,k,V,lt", [(60, 10, 70000, "f32"), (1100, 1, 20000, "f32"), (260, 8, 40000, "bf16")])
+def test_long_rows_tokens_only(B, k, V, lt):
+    # no p_j(x_j) outputs: rows after the first rejection stop early (and help it, where
+    # the batch allows); two calls on one workspace, which must come back clear
+    import speculative_sampling_verify_03_amd as sv
+    case = linear_case(B, k, V, seed=B + k, dtype=lt, noise_sigma=0.5 if k > 8 else 1.0)
+    ws = sv.new_workspace(sv.SV_KIND_LINEAR, B, k, V)
+    for rep in range(2):
+        _run(case, 21 + rep, f"long rows tokens only B={B} k={k} V={V} call {rep}", ws=ws, offset=rep,
+             with_probs=False)
+        assert status_word(ws) == 0
+        assert sections_clear(ws, sv.SV_KIND_LINEAR, case.k, V), f"call {rep}: workspace not cleared"
 
 
 def test_long_rows_invalid_tokens_and_minus_inf():
