@@ -40,6 +40,9 @@ struct RowParams {
   uint64_t* help_words;    // per row help_stride words: (m, Z), tile claims, unit totals
   int32_t help_stride;
   int32_t help_on;
+  int32_t bonus_wait;      // set by the launcher: the last row of a sequence waits for the
+                           //     earlier rows' decisions before it streams (help_on grids
+                           //     that run in one round)
   uint32_t* errword;       // sticky: set when a wait for another workgroup ran out
   // every word above except errword is zero on entry and is returned to zero before the
   // kernel ends

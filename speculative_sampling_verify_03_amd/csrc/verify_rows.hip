@@ -86,6 +86,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   __shared__ float s_slot[NV];    // a cooperatively recomputed unit's slot totals
   __shared__ int s_claim[2], s_hr, s_help;  // residual tiles claimed; the row this one helps
   __shared__ int s_quit[NT / kWave];        // per wave: stopped streaming (below)
+  __shared__ int s_pre;                     // the last row: an earlier row rejected (below)
   __shared__ float s_hm, s_hz;                      // the helped row's (max, sum)
   __shared__ float s_usmp;
   __shared__ int8_t s_par[64], s_fc[64], s_nc[64], s_dep[64];
@@ -182,18 +183,39 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   // and keep streaming.)
   const bool may_quit = QUIT && j > 0 && (j == P.k || (P.out_tprob == nullptr && P.out_aprob == nullptr));
   bool quit = false;
+  // In a grid that runs in one round (bonus_wait, set by the launcher) the last row of a
+  // sequence waits for the earlier rows' decisions before it streams: it is needed only
+  // when all of them kept their drafts, and otherwise helps the earliest rejected row at
+  // once, while the earlier rows have the bandwidth to themselves meanwhile.
+  bool pre_quit = false;
+  if (HELP && !PIPE && P.bonus_wait && j == P.k) {
+    if (tid == 0) {
+      uint64_t* dm = P.help_words + static_cast<size_t>(b * P.R) * P.help_stride + (P.help_stride - 1);
+      const uint64_t low = (1ull << j) - 1ull;
+      uint64_t v = 0;
+      for (int spin = 0; spin < kHelpSpin && (v & low) != low; ++spin)
+        v = __hip_atomic_load(dm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v & low) != low) __hip_atomic_fetch_or(P.errword, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a row marks its decision after its rejection has been published
+      const uint64_t seen = __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_pre = seen > static_cast<uint64_t>(64 - j) ? 1 : 0;
+    }
+    __syncthreads();
+    pre_quit = s_pre != 0;
+  }
+  const int stream_tiles = pre_quit ? 0 : P.ntiles;
   if (PIPE) load_tile(buf, 0);
-  for (int tile = 0; tile < P.ntiles; ++tile) {
+  for (int tile = 0; tile < stream_tiles; ++tile) {
     const int v0 = tile * TILE + wid * (NV * kWave) + lane;
     // every load of the tile is in flight before the first edge mask
     if (!PIPE) load_tile(buf, tile);
+    else if (tile + 1 < P.ntiles) load_tile(nxt, tile + 1);
     uint64_t chk = 0;
     if (QUIT) {  // every row reads it (a branch around the load made the compiler wait for
                  // it before the next tile's loads)
       asm volatile("" ::: "memory");  // issued behind the tile's loads
       chk = __hip_atomic_load(&P.seqword[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    else if (tile + 1 < P.ntiles) load_tile(nxt, tile + 1);
     // Linear rows of several waves: the pair of position j is the same for every thread,
     // so every thread draws it in uniform control flow (scalar instructions) while the
     // tile's loads are in flight, instead of one lane of wave 0 spending some 300 vector
@@ -266,7 +288,7 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
   pin_packed(buf);  // pass 2 starts again from the packed row
   if (may_quit && lane == 0) s_quit[wid] = quit ? 1 : 0;
   __syncthreads();
-  bool row_quit = false;
+  bool row_quit = pre_quit;
   if (may_quit) {
 #pragma unroll
     for (int w = 0; w < NT / kWave; ++w) row_quit = row_quit || s_quit[w] != 0;
@@ -1113,25 +1135,31 @@ static hipError_t launch_one(const RowParams& P, const TreeDesc& td, int grid, h
 // 46.8 us), so that grid runs the instance without them.
 template <bool BF16, bool TREE, int QMODE>
 static hipError_t launch_tiles_256(const RowParams& P, const TreeDesc& td, int grid, hipStream_t st) {
-  if (TREE) return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
-  static int cap[64] = {};  // workgroups of the instance the device holds at once, per device
-  int dev = 0, c = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    c = __atomic_load_n(&cap[dev], __ATOMIC_RELAXED);
-    if (c == 0) {
-      const size_t lds = 3 * static_cast<size_t>(P.ntiles) * (256 / kWave) * sizeof(float);
-      int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, row_verify_kernel<BF16, 256, 16, TREE, QMODE, true>,
-                                                       256, lds) == hipSuccess &&
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
-          cus > 0) {
-        c = per_cu * cus;
-        __atomic_store_n(&cap[dev], c, __ATOMIC_RELAXED);
+  if constexpr (TREE) return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
+  else {
+    static int cap[64] = {};  // workgroups of the instance the device holds at once, per device
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+      c = __atomic_load_n(&cap[dev], __ATOMIC_RELAXED);
+      if (c == 0) {
+        const size_t lds = 3 * static_cast<size_t>(P.ntiles) * (256 / kWave) * sizeof(float);
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, row_verify_kernel<BF16, 256, 16, TREE, QMODE, true>,
+                                                         256, lds) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
+            cus > 0) {
+          c = per_cu * cus;
+          __atomic_store_n(&cap[dev], c, __ATOMIC_RELAXED);
+        }
       }
     }
+    if (c > 0 && grid > c) return launch_one<BF16, 256, 16, TREE, QMODE, true>(P, td, grid, st);
+    // one round: the last rows wait for the earlier rows' decisions when those fill the
+    // chip's CUs on their own (B k >= 256, so their stream keeps HBM busy meanwhile)
+    RowParams P1 = P;
+    P1.bonus_wait = c > 0 && P.help_on && P.k > 0 && static_cast<int64_t>(P.B) * P.k >= 256;
+    return launch_one<BF16, 256, 16, TREE, QMODE>(P1, td, grid, st);
   }
-  if (c > 0 && grid > c) return launch_one<BF16, 256, 16, TREE, QMODE, true>(P, td, grid, st);
-  return launch_one<BF16, 256, 16, TREE, QMODE>(P, td, grid, st);
 }
 
 template <bool BF16, bool TREE, int QMODE>

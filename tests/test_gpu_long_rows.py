@@ -67,6 +67,23 @@ def test_long_rows_tokens_only(B, k, V, lt):
         assert sections_clear(ws, sv.SV_KIND_LINEAR, case.k, V), f"call {rep}: workspace not cleared"
 
 
+@pytest.mark.parametrize("B,k,V,lt,with_probs", [(64, 4, 70000, "bf16", True), (64, 4, 70000, "bf16", False),
+                                                 (128, 2, 40000, "f32", True)])
+def test_long_rows_last_row_waits(B, k, V, lt, with_probs):
+    # one round of workgroups with B k >= 256: each sequence's last row waits for the
+    # earlier rows' decisions and streams only when all of them kept their drafts, else it
+    # helps the rejected row at once
+    import speculative_sampling_verify_03_amd as sv
+    case = linear_case(B, k, V, seed=B * k, dtype=lt, noise_sigma=0.7)
+    ws = sv.new_workspace(sv.SV_KIND_LINEAR, B, k, V)
+    for rep in range(2):
+        _, ref = _run(case, 31 + rep, f"long rows, last row waits, B={B} k={k} V={V} call {rep}", ws=ws,
+                      offset=rep, with_probs=with_probs)
+        assert status_word(ws) == 0
+        assert sections_clear(ws, sv.SV_KIND_LINEAR, case.k, V), f"call {rep}: workspace not cleared"
+    assert (ref["accept_len"] < k).sum() > 0 and (ref["accept_len"] == k).sum() > 0
+
+
 def test_long_rows_invalid_tokens_and_minus_inf():
     V = 140000
     case = linear_case(16, 4, V, seed=5, dtype="bf16", noise_sigma=1.0)
