@@ -109,6 +109,7 @@ int run_rows(bool tree, bool lossless, const void* logits, int lt, const void* p
     P.tree_skip = 1;
     for (int u = 0; u < ti->N; ++u)
       if (ti->nchild[u] > 31) P.tree_skip = 0;
+    P.leaf_wait = P.tree_skip && lossless;
   }
   // How the residual reads q rows (see launch_rows): every logits row must have the same
   // 16-byte phase (whole-vector pitch), and the matching q chunks must line up with it.

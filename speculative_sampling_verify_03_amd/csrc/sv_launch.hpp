@@ -35,6 +35,9 @@ struct RowParams {
                            //     first child)
   int32_t tree_skip;       // tree: nodes off every accepted path skip their draw (every
                            //     node has at most 31 children)
+  int32_t leaf_wait;       // lossless tree (with tree_skip): a leaf streams its row only
+                           //     after its parent kept it and no decided node above
+                           //     dropped its path
   // Linear multi-tile rows (help_on): the rows after a sequence's earliest rejection
   // compute residual tiles of that rejected row (verify_rows.hip).
   uint64_t* help_words;    // per row help_stride words: (m, Z), tile claims, unit totals

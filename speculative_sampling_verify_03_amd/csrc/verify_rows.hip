@@ -203,6 +203,49 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     __syncthreads();
     pre_quit = s_pre != 0;
   }
+  // Lossless trees (leaf_wait, with tree_skip): every node keeps at most one child, so one
+  // path is kept and a leaf's row serves only the extra token, drawn at the path's end.  A
+  // leaf waits (one lane, bounded) for its parent's decisions and streams only when the
+  // parent kept it and no decided node above dropped its path; the inner nodes, dispatched
+  // before the leaves, have the bandwidth meanwhile.  (With independent tests per child,
+  // many leaves stay kept and then stream late: that tree measured slower this way.)
+  if (TREE && P.leaf_wait && j > 0 && s_nc[j] == 0) {
+    if (wid == 0) {
+      const int N = P.R;
+      uint64_t* rw = P.rowword + static_cast<size_t>(b) * N;
+      const int pa = s_par[j];
+      int off = 0;
+      if (lane == 0) {
+        uint64_t w = 0;
+        for (int spin = 0; spin < kHelpSpin && (w >> 63) == 0; ++spin)
+          w = __hip_atomic_load(rw + pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> 63) == 0) __hip_atomic_fetch_or(P.errword, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else off = (((w >> 32) >> (j - s_fc[pa])) & 1ull) == 0 ? 1 : 0;
+      }
+      off = __shfl(off, 0);
+      if (!off) {  // the path above the parent: every node's word, one per lane
+        uint64_t w = 0;
+        if (lane < N) w = __hip_atomic_load(rw + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool decided = lane < N && (w >> 63) != 0;
+        uint64_t kept = 0;
+        if (decided) kept = ((w >> 32) & ((1ull << s_nc[lane]) - 1ull)) << s_fc[lane];
+        const uint64_t dmask = __ballot(decided);
+        uint32_t klo = static_cast<uint32_t>(kept), khi = static_cast<uint32_t>(kept >> 32);
+        for (int o = 32; o >= 1; o >>= 1) {
+          klo |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(klo), o));
+          khi |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(khi), o));
+        }
+        const uint64_t amask = (static_cast<uint64_t>(khi) << 32) | klo;
+        for (int x = pa; x != 0; x = s_par[x]) {
+          const int px = s_par[x];
+          if (((dmask >> px) & 1ull) != 0 && ((amask >> x) & 1ull) == 0) off = 1;
+        }
+      }
+      if (lane == 0) s_pre = off;
+    }
+    __syncthreads();
+    pre_quit = s_pre != 0;
+  }
   const int stream_tiles = pre_quit ? 0 : P.ntiles;
   if (PIPE) load_tile(buf, 0);
   for (int tile = 0; tile < stream_tiles; ++tile) {
@@ -429,7 +472,8 @@ void row_verify_kernel(RowParams P, TreeDesc td) {
     }
     s_flag = cand;
   }
-  if (TREE && P.tree_skip && wid == 0) {
+  if (TREE && pre_quit && tid == 0) s_flag = 0;  // a leaf off every kept path: no draw
+  if (TREE && P.tree_skip && !pre_quit && wid == 0) {
     // A node publishes its children's decisions at once (bit 63 of its row word, the kept
     // children above bit 32, relative to its first child; its drawn token joins the low
     // half later).  A node that would draw first reads every node's word: the token is
