@@ -213,7 +213,16 @@ int spec_verify_greedy(const void* target_logits, int lt, const int32_t* draft_t
     P.flat = 1;
     P.nvec = static_cast<int32_t>(nvec);
     P.G = static_cast<int32_t>(G < 1 ? 1 : G);
+    // Two launches (the first two positions of every sequence, then the rest of the
+    // sequences that kept both) when the tensor is larger than one round of pieces of the
+    // minimum size would cover twice over.
+    constexpr int kFirstPositions = 2;
+    if (k + 1 > kFirstPositions && total >= int64_t(2) * sv::kGreedyFlatMaxGroups * sv::kGreedyFlatMinVectors) {
+      P.phase = 1;
+      P.P0 = kFirstPositions;
+    }
   }
+  P.alive = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.seq_off);
   P.out_tokens = out_tokens;
   P.out_accept_len = out_accept_len;
   P.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.counters_off);

@@ -117,6 +117,12 @@ struct GreedyParams {
   int32_t* out_accept_len;
   uint32_t* counters;  // [B] arrival tickets (zero on entry and exit)
   uint64_t* rowword;   // [B * R] orderable (value, lowest index) key of each row's maximum
+  // flat path in two launches (phase 1, then 2; phase 0 = one launch over every row):
+  // phase 1 covers positions 0 .. P0-1 of every sequence, phase 2 positions P0 .. k of the
+  // sequences that kept all of their first P0 drafts, listed by phase 1
+  int32_t phase, P0;
+  uint32_t* alive;     // [B] sequences left for phase 2, then their count, then phase 2's
+                       //     workgroup tickets (zero on entry and exit)
 };
 constexpr int kGreedyThreads = 256;
 constexpr int kGreedyUnroll = 8;

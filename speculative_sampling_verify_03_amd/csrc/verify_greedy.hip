@@ -18,6 +18,7 @@
 namespace sv {
 
 __device__ void greedy_finish(const GreedyParams& P, int b, int lane);
+__device__ void greedy_first_positions(const GreedyParams& P, int b, int lane);
 
 template <bool BF16>
 __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams P) {
@@ -166,20 +167,32 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParam
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
   const int64_t nvec = P.nvec;
-  const int64_t total = static_cast<int64_t>(P.B) * P.R * nvec;
+  // The rows of this launch, numbered t = a * RP + jj: phase 0 every row, phase 1 the first
+  // P0 positions of every sequence, phase 2 the later positions of the listed sequences.
+  const int phase = P.phase;
+  const int RP = phase == 0 ? P.R : phase == 1 ? P.P0 : P.R - P.P0;
+  const int j0 = phase == 2 ? P.P0 : 0;
+  uint32_t* const nalive = P.alive + P.B;
+  int64_t nseq = P.B;
+  if (phase == 2) nseq = __hip_atomic_load(nalive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t total = nseq * RP * nvec;
   const int64_t beg = total * blockIdx.x / P.G;
   const int64_t end = total * (blockIdx.x + 1) / P.G;
   const SV_GLOBAL Vec16* base = gptr<Vec16>(P.logits);
-  const uint32_t seq_vectors = static_cast<uint32_t>(P.R * nvec);
+  // a sequence's vectors counted when this launch's share of it is done
+  const uint32_t seq_vectors = static_cast<uint32_t>((phase == 1 ? P.P0 : P.R) * nvec);
 
   int64_t pos = beg;
-  int64_t r = beg / nvec;
+  int64_t t = beg / nvec;
   while (pos < end) {
-    const int64_t row0 = r * nvec;
+    const int64_t row0 = t * nvec;
     const int64_t piece_end = min(end, row0 + nvec);
     const int n = static_cast<int>(piece_end - pos);    // vectors in this piece
     const int first = static_cast<int>(pos - row0);     // its first vector inside the row
-    const SV_GLOBAL Vec16* pp = base + pos;
+    const int64_t a = t / RP;
+    const int b = phase == 2 ? static_cast<int>(P.alive[a]) : static_cast<int>(a);
+    const int64_t r = static_cast<int64_t>(b) * P.R + j0 + (t - a * RP);
+    const SV_GLOBAL Vec16* pp = base + r * nvec + first;
     // Per thread: the largest vector maximum, the first of this thread's vectors (they
     // ascend) that reaches it, and that vector's data; the element index is looked up once
     // at the end.  A max per element instead of a (value, index) compare and select.
@@ -217,7 +230,6 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParam
       s_i[wid] = bi;
     }
     __syncthreads();
-    const int b = static_cast<int>(r / P.R);
     if (tid == 0) {
       float v = s_v[0];
       int i = s_i[0];
@@ -228,9 +240,58 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParam
       s_last = prev + static_cast<uint32_t>(n) == seq_vectors;
     }
     __syncthreads();  // also: s_v is rewritten by the next piece only after this
-    if (s_last && wid == 0) greedy_finish(P, b, lane);
+    if (s_last && wid == 0) {
+      if (phase == 1) greedy_first_positions(P, b, lane);
+      else greedy_finish(P, b, lane);
+    }
     pos = piece_end;
-    ++r;
+    ++t;
+  }
+  if (phase == 2) {
+    // the last workgroup of phase 2 clears the list, its count and these tickets (every
+    // workgroup has read the list before taking its ticket)
+    if (tid == 0) s_last = take_ticket(nalive + 1) == static_cast<uint32_t>(P.G - 1);
+    __syncthreads();
+    if (s_last && wid == 0) {
+      for (int64_t q = lane; q < nseq; q += kWave)
+        __hip_atomic_store(&P.alive[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) {
+        reset_ticket(nalive);
+        reset_ticket(nalive + 1);
+      }
+    }
+  }
+}
+
+// Phase 1's last arrival for sequence b (positions 0 .. P0-1 done, P0 <= k): a mismatch
+// among them ends the sequence here (outputs, its words cleared); otherwise it is listed
+// for phase 2, whose last arrival reads every row's key.  One wave.
+__device__ void greedy_first_positions(const GreedyParams& P, int b, int lane) {
+  const int P0 = P.P0;
+  uint64_t* keys = P.rowword + static_cast<size_t>(b) * P.R;
+  int g = -1, x = -1;
+  if (lane < P0) {
+    g = argmax_key_index(__hip_atomic_load(keys + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    x = gptr<int32_t>(P.tokens)[static_cast<size_t>(b) * P.k + lane];
+  }
+  const uint64_t miss = __ballot(lane < P0 && g != x);
+  if (miss) {
+    const int n = __ffsll(static_cast<long long>(miss)) - 1;
+    const int y = lane_value(g, n);
+    if (lane < P.R) {
+      int tk = -1;
+      if (lane < n) tk = x;
+      else if (lane == n) tk = y;
+      P.out_tokens[static_cast<size_t>(b) * P.R + lane] = tk;
+    }
+    if (lane < P0) (void)atomic_xchg_u64(keys + lane, 0ull);
+    if (lane == 0) {
+      P.out_accept_len[b] = n;
+      reset_ticket(&P.counters[b]);
+    }
+  } else if (lane == 0) {
+    const uint32_t at = __hip_atomic_fetch_add(P.alive + P.B, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&P.alive[at], static_cast<uint32_t>(b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -261,10 +322,30 @@ hipError_t launch_greedy(const GreedyParams& P0, bool bf16, hipStream_t st) {
     // one round: no more workgroups than the chip holds at once
     GreedyParams P = P0;
     const int resident = flat_resident_groups(bf16);
-    if (resident > 0 && P.G > resident) P.G = resident;
-    if (bf16) hipLaunchKernelGGL(greedy_flat_kernel<true>, dim3(P.G), dim3(kGreedyThreads), 0, st, P);
-    else hipLaunchKernelGGL(greedy_flat_kernel<false>, dim3(P.G), dim3(kGreedyThreads), 0, st, P);
-    return hipGetLastError();
+    auto run = [&](GreedyParams& Q) {
+      if (bf16) hipLaunchKernelGGL(greedy_flat_kernel<true>, dim3(Q.G), dim3(kGreedyThreads), 0, st, Q);
+      else hipLaunchKernelGGL(greedy_flat_kernel<false>, dim3(Q.G), dim3(kGreedyThreads), 0, st, Q);
+      return hipGetLastError();
+    };
+    if (P.phase == 0) {
+      if (resident > 0 && P.G > resident) P.G = resident;
+      return run(P);
+    }
+    // Two launches: the first P0 positions of every sequence, then the rest of the
+    // sequences that kept all of them (the sequential rule stops at the first mismatch,
+    // so the later rows of the others are never read).  Phase 2 does not know its size
+    // on the host: it takes the whole resident grid and each workgroup reads the count.
+    const int64_t total1 = static_cast<int64_t>(P.B) * P.P0 * P.nvec;
+    int64_t G1 = (total1 + kGreedyFlatMinVectors - 1) / kGreedyFlatMinVectors;
+    const int cap = resident > 0 ? resident : kGreedyFlatMaxGroups;
+    if (G1 > cap) G1 = cap;
+    P.phase = 1;
+    P.G = static_cast<int32_t>(G1 < 1 ? 1 : G1);
+    hipError_t e = run(P);
+    if (e != hipSuccess) return e;
+    P.phase = 2;
+    P.G = cap;
+    return run(P);
   }
   const GreedyParams& P = P0;
   const int grid = P.B * P.R * P.S;

@@ -142,3 +142,44 @@ def test_greedy_edge_vector_ties(misalign):
     got = run_greedy(L, X, misalign)
     assert list(got["accept_len"]) == [3, 2, 3, 2]
     check_greedy(got, L, X, what=f"greedy edge ties misalign={misalign}")
+
+
+@pytest.mark.parametrize("dtype,B,k,V", [("bf16", 260, 8, 40000), ("f32", 120, 8, 40000), ("bf16", 700, 2, 40000)])
+def test_greedy_flat_two_launches(dtype, B, k, V):
+    """Large aligned tensors run the flat path in two launches: the first two positions of
+    every sequence, then the later positions of the sequences that kept both.  Ties at
+    equal maxima, signed zeros, random rows and accept lengths from 0 to k; two calls on
+    one workspace, which must come back clear."""
+    from gpu_common import sections_clear, status_word
+    import speculative_sampling_verify_03_amd as sv
+    R = k + 1
+    rng = np.random.default_rng(B + k + V)
+    L = np.full((B, R, V), -1.0, dtype=np.float32)
+    kinds = rng.integers(0, 3, size=(B, R))
+    for b in range(B):
+        for j in range(R):
+            if kinds[b, j] == 0:
+                L[b, j] = rng.normal(size=V).astype(np.float32)
+            elif kinds[b, j] == 1:
+                L[b, j, rng.choice(V, size=3, replace=False)] = 3.0
+            else:
+                i1, i2 = sorted(rng.choice(V, size=2, replace=False))
+                L[b, j, i1] = -0.0
+                L[b, j, i2] = 0.0
+    Lt = torch.from_numpy(L).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    g = np.argmax(Lt.float().numpy(), axis=-1)
+    keep = rng.random((B, k)) < 0.8
+    X = torch.from_numpy(np.where(keep, g[:, :k], (g[:, :k] + 1) % V).astype(np.int32))
+    lg = Lt.to("cuda")
+    ws = sv.new_workspace(sv.SV_KIND_GREEDY, B, k, V)
+    for call in range(2):
+        announce(f"greedy flat, two launches: B={B} k={k} V={V} {dtype} call {call}")
+        out = dict(tokens=torch.full((B, R), -7, dtype=torch.int32, device="cuda"),
+                   accept_len=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+        sv.spec_verify_greedy(lg, X.to("cuda"), out["tokens"], out["accept_len"], ws)
+        torch.cuda.synchronize()
+        got = {n: t.cpu().numpy() for n, t in out.items()}
+        ref = check_greedy(got, Lt, X, what=f"greedy two launches B={B} k={k} V={V} {dtype} call {call}")
+        assert status_word(ws) == 0
+        assert sections_clear(ws, sv.SV_KIND_GREEDY, k, V), f"call {call}: workspace not cleared"
+    assert (ref["accept_len"] < 2).sum() > 0 and (ref["accept_len"] >= 2).sum() > 0
