@@ -196,8 +196,20 @@ class Greedy(Linear):
         self.sets = [(lg, q, self.cases[ci].greedy_tokens.cuda(), ci) for lg, q, x, ci in self.sets]
 
     def algorithmic_bytes(self):
+        # The rows the sequential rule examines: positions 0..n of every sequence (n its
+        # accept length), counted on the inputs and averaged over the input sets; the kernels
+        # read no row after a sequence's first mismatch once they know of it, so counting
+        # every row would put the figure above what the chip can stream.
+        if not hasattr(self, "_examined"):
+            rows = []
+            for c in self.cases:
+                g = c.logits.float().argmax(dim=-1).numpy()
+                miss = g[:, :self.k] != c.greedy_tokens.numpy()
+                n = np.where(miss.any(axis=1), miss.argmax(axis=1), self.k)
+                rows.append(float((n + 1).sum()))
+            self._examined = sum(rows) / len(rows)
         el = self.cases[0].logits.element_size()
-        return self.B * self.R * self.V * el + self.B * self.k * 4 + self.B * self.R * 4 + self.B * 4
+        return int(self._examined * self.V * el) + self.B * self.k * 4 + self.B * self.R * 4 + self.B * 4
 
     def oracle_sample(self, budget_s):
         from oracle import verify_greedy
