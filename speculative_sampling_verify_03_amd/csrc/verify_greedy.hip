@@ -151,7 +151,10 @@ __device__ void greedy_finish(const GreedyParams& P, int b, int lane) {
 // range is walked in pieces that end at row boundaries; each piece's (value, lowest index)
 // goes into its row's key word with one atomic max, and its vector count into the
 // sequence's counter, so the piece that brings the count to R * nvec is the sequence's
-// last and writes its outputs.
+// last and writes its outputs.  Large tensors take two launches of this kernel (phase 1:
+// positions 0 and 1 of every sequence; phase 2: the later positions of the sequences that
+// kept both, listed by phase 1), since the rows after a sequence's first mismatch are never
+// examined by the sequential rule.
 template <bool BF16>
 __global__ __launch_bounds__(kGreedyThreads) void greedy_flat_kernel(GreedyParams P) {
   using E = Elem<BF16>;
